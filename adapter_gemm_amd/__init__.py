@@ -1,0 +1,202 @@
+"""Python binding of liblora (argument marshalling only).
+
+Every step of the layer runs in the HIP kernels behind the C-ABI declared in
+include/lora.h; this module turns torch tensors into pointers, sizes and the
+current HIP stream, calls the library and raises on a non-zero status.  There
+is no fallback: if liblora.so is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora.so")
+
+# status codes / enums (mirror include/lora.h)
+LORA_OK, LORA_E_ARG, LORA_E_ID, LORA_E_RANK, LORA_E_DTYPE, LORA_E_ALIGN, LORA_E_HIP, LORA_E_SIZE = range(8)
+F32, BF16, FP8_E4M3 = 0, 1, 2
+LAUNCH_EXACT, LAUNCH_PERSISTENT, LAUNCH_BUCKETED, LAUNCH_FULL_BATCH = 0, 1, 2, 3
+FLAG_ACT_QUANT_E4M3 = 0x1
+MAX_RANK = 128
+DEV_MAX_SLOTS = 8192
+TILE_SMALL, TILE_LARGE = 16, 64
+SEG_HEADER = 16
+
+EXPORTED = [
+    "lora_segment_words", "lora_build_segments", "lora_plan_segments", "lora_build_segments_dev",
+    "lora_shrink", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
+    "lora_quantize_e4m3", "lora_status_string", "lora_last_error",
+]
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.lora_status_string(status).decode()
+        if status == LORA_E_HIP:
+            msg += ": " + _lib.lora_last_error().decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("slot_rank", ctypes.c_void_p),
+                ("slot_scale", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("r_cap", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
+
+
+class BaseDesc(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("ld_w", ctypes.c_int32)]
+
+
+class Summary(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_active", "n_segments", "m_max", "row_bound", "n_tiles_small", "n_tiles_large", "T", "error")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m adapter_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "lora_segment_words": (SZ, [I32]),
+        "lora_plan_segments": (I32, [P, P, I32, I32, I32, P, P]),
+        "lora_build_segments": (I32, [P, P, I32, I32, I32, P, P, P, P]),
+        "lora_build_segments_dev": (I32, [P, P, I32, I32, I32, P, P]),
+        "lora_shrink": (I32, [P, P, I32, P, P, I32, P, I32, I32, P]),
+        "lora_expand": (I32, [P, P, I32, P, P, I32, P, I32, I32, I32, P]),
+        "lora_fused_linear": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P, SZ, P]),
+        "lora_fused_workspace_bytes": (SZ, [I32, I32, I32]),
+        "lora_quantize_e4m3": (I32, [P, I32, I32, I32, P, I32, P, P]),
+        "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "lora_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != LORA_OK:
+        raise LoraError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3,
+            torch.float8_e4m3fn: FP8_E4M3}[t.dtype]
+
+
+def pool_desc(A, B, slot_rank, slot_scale) -> PoolDesc:
+    """A [N, r_cap, d_in], B [N, d_out, r_cap] (fp32 or bf16), slot_rank int32 [N],
+    slot_scale fp32 [N], all on the device."""
+    N, r_cap, d_in = A.shape
+    d_out = B.shape[1]
+    return PoolDesc(A.data_ptr(), B.data_ptr(), slot_rank.data_ptr(), slot_scale.data_ptr(), _dtype_code(A),
+                    N, r_cap, d_in, d_out)
+
+
+def base_desc(W, w_scale=None) -> BaseDesc:
+    """W [d_out, ld_w] fp32 / bf16 / uint8 e4m3 codes; w_scale fp32 [d_out] for fp8."""
+    return BaseDesc(W.data_ptr(), _ptr(w_scale), _dtype_code(W), W.stride(0))
+
+
+def segment_words(T: int) -> int:
+    return int(_lib.lora_segment_words(T))
+
+
+def plan_segments(ids, active, n_slots: int, order: int = 0):
+    """Host-only grouping (numpy int32 ids / uint8 active) -> (plan int32 array, summary dict)."""
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T = int(ids.shape[0])
+    act = None if active is None else np.ascontiguousarray(active, dtype=np.uint8)
+    plan = np.zeros(segment_words(T), dtype=np.int32)
+    s = Summary()
+    _check(_lib.lora_plan_segments(ids.ctypes.data, None if act is None else act.ctypes.data, T, n_slots, order,
+                                   plan.ctypes.data, ctypes.byref(s)), "lora_plan_segments")
+    return plan, s.as_dict()
+
+
+def build_segments(ids, active, n_slots: int, seg, staging, order: int = 0, stream=None) -> Summary:
+    """Host ids (CPU int32 tensor) -> device segment buffer `seg`; `staging` is a
+    host int32 tensor of segment_words(T) words (pinned for an asynchronous copy)."""
+    T = int(ids.shape[0])
+    s = Summary()
+    _check(_lib.lora_build_segments(_ptr(ids), _ptr(active), T, n_slots, order, staging.data_ptr(),
+                                    seg.data_ptr(), ctypes.byref(s), _stream(stream)), "lora_build_segments")
+    return s
+
+
+def build_segments_dev(ids, active, n_slots: int, seg, order: int = 0, stream=None) -> None:
+    T = int(ids.shape[0])
+    _check(_lib.lora_build_segments_dev(_ptr(ids), _ptr(active), T, n_slots, order, seg.data_ptr(),
+                                        _stream(stream)), "lora_build_segments_dev")
+
+
+def shrink(pool: PoolDesc, seg, T: int, summary: Optional[Summary], x, v, launch: int = LAUNCH_EXACT,
+           stream=None) -> None:
+    _check(_lib.lora_shrink(ctypes.byref(pool), seg.data_ptr(), T,
+                            None if summary is None else ctypes.byref(summary), x.data_ptr(), x.stride(0),
+                            v.data_ptr(), v.stride(0), launch, _stream(stream)), "lora_shrink")
+
+
+def expand(pool: PoolDesc, seg, T: int, summary: Optional[Summary], v, y, launch: int = LAUNCH_EXACT,
+           stream=None) -> None:
+    _check(_lib.lora_expand(ctypes.byref(pool), seg.data_ptr(), T,
+                            None if summary is None else ctypes.byref(summary), v.data_ptr(), v.stride(0),
+                            y.data_ptr(), _dtype_code(y), y.stride(0), launch, _stream(stream)), "lora_expand")
+
+
+def fused_workspace_bytes(T: int, d_in: int, flags: int) -> int:
+    return int(_lib.lora_fused_workspace_bytes(T, d_in, flags))
+
+
+def fused_linear(base: BaseDesc, pool: Optional[PoolDesc], seg, x, v, y, flags: int = 0, workspace=None,
+                 stream=None) -> None:
+    T, d_in = int(x.shape[0]), int(x.shape[1])
+    d_out = int(y.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lora_fused_linear(ctypes.byref(base), None if pool is None else ctypes.byref(pool), _ptr(seg), T,
+                                  x.data_ptr(), x.stride(0), _ptr(v), 0 if v is None else v.stride(0),
+                                  y.data_ptr(), y.stride(0), d_in, d_out, flags, _ptr(workspace), ws_bytes,
+                                  _stream(stream)), "lora_fused_linear")
+
+
+def quantize_e4m3(x, q, s_x, stream=None) -> None:
+    T, d = int(x.shape[0]), int(x.shape[1])
+    _check(_lib.lora_quantize_e4m3(x.data_ptr(), T, d, x.stride(0), q.data_ptr(), q.stride(0), s_x.data_ptr(),
+                                   _stream(stream)), "lora_quantize_e4m3")
+
+
+def summary_from_words(words) -> Summary:
+    """Summary struct from the first words of a segment buffer (host copy)."""
+    s = Summary()
+    for k, (n, _) in enumerate(Summary._fields_):
+        setattr(s, n, int(words[k]))
+    return s

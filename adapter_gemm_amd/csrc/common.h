@@ -1,0 +1,110 @@
+// Internal definitions shared by the HIP kernels and the C-ABI layer of
+// liblora (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora.h"
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// segment buffer layout (documented in lora.h)
+// ---------------------------------------------------------------------------
+constexpr int kSegHeader = 16;
+enum SummaryWord {
+  kNActive = 0, kNSegments = 1, kMMax = 2, kRowBound = 3,
+  kNTilesSmall = 4, kNTilesLarge = 5, kRows = 6, kError = 7
+};
+
+struct SegPtrs {
+  int32_t* sum;
+  int32_t* perm;
+  int32_t* pos_seg;
+  int32_t* seg_start;
+  int32_t* seg_adapter;
+  int32_t* tiles_small;
+  int32_t* tiles_large;
+};
+
+__host__ __device__ inline SegPtrs seg_ptrs(int32_t* base, int T) {
+  SegPtrs p;
+  p.sum = base;
+  p.perm = base + kSegHeader;
+  p.pos_seg = p.perm + T;
+  p.seg_start = p.pos_seg + T;
+  p.seg_adapter = p.seg_start + (T + 1);
+  p.tiles_small = p.seg_adapter + T;
+  p.tiles_large = p.tiles_small + 2 * T;
+  return p;
+}
+
+__host__ __device__ inline size_t seg_words(int T) { return (size_t)kSegHeader + 8 * (size_t)T + 1; }
+
+// A segment buffer is usable only if its build succeeded and covered T rows;
+// otherwise kernels treat the batch as having no live rows, in batch order.
+__device__ __forceinline__ bool seg_valid(const SegPtrs& P, int T) {
+  return P.sum[kError] == 0 && P.sum[kRows] == T;
+}
+
+// ---------------------------------------------------------------------------
+// vector types
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// 128-bit global loads / stores
+__device__ __forceinline__ u32x4_t ld128(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void st128(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (threadIdx.x & 63) ? (~0ull >> (64 - (threadIdx.x & 63))) : 0ull;
+}
+
+// ---------------------------------------------------------------------------
+// host-side argument bundles for the kernel launchers
+// ---------------------------------------------------------------------------
+struct LaunchShape {
+  int mode;          // LORA_LAUNCH_*
+  int n_tiles;       // host summary (EXACT), else unused
+  int row_bound;     // host summary (BUCKETED)
+  int slots;         // L for BUCKETED / FULL_BATCH = min(T, n_slots)
+};
+
+hipError_t launch_build_segments(const int32_t* ids, const uint8_t* active, int T, int n_slots, int order,
+                                 int32_t* seg, hipStream_t st);
+
+hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const LaunchShape& ls,
+                         const void* x, int ld_x, float* v, int ld_v, hipStream_t st);
+
+hipError_t launch_expand(const lora_pool_t& pool, int32_t* seg, int T, const LaunchShape& ls,
+                         const float* v, int ld_v, void* y, int y_dtype, int ld_y, hipStream_t st);
+
+hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_t* seg, int T,
+                        const void* x, int ld_x, const float* v, int ld_v, void* y, int ld_y, int d_in,
+                        int d_out, int flags, void* workspace, hipStream_t st);
+
+hipError_t launch_quantize_e4m3(const void* x, int T, int d, int ld_x, uint8_t* q, int ld_q, float* s_x,
+                                hipStream_t st);
+
+}  // namespace lora

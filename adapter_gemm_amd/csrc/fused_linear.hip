@@ -1,0 +1,521 @@
+// Fused linear: y[i, n] = epi( sum_k x[i, k] W0[n, k] ) with the adapter
+// up-projection added in the epilogue ("EpiLoRA" 3.1 and Fig. 10, kernel K2:
+// a GEMM over adapter-sorted rows whose epilogue, for each adapter group in
+// the output tile, adds h_l B_l^T reading only the tile's slice of B_l, then
+// writes the rows back in token order).
+//
+// gfx950 design
+//  * Rows are taken in the grouped order (perm), so an output tile meets only
+//    a few contiguous adapter groups; x rows are gathered through perm while
+//    they are staged, and results are scattered back through perm.
+//  * Main loop: 256 threads = 4 waves in a 2 x 2 grid; each k-step stages a
+//    BM x 128-byte slab of x and a BN x 128-byte slab of W0 in LDS (double
+//    buffered, 16-byte chunks XOR-swizzled by row), and each wave issues
+//    v_mfma_f32_16x16x32_bf16 (bf16 base, or fp8 codes widened to bf16 while
+//    staging: W8A16) or v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 x fp8: W8A8).
+//  * Epilogue: base scales (fp8: w_scale[n], W8A8 also s_x[i]); then, per
+//    adapter group intersecting the wave's rows, the rank-r product
+//    (s_a v) B_a^T runs on the same MFMA accumulators, with v rows of other
+//    groups masked to zero.  Operand fragments come straight from global
+//    memory: a lane's 8 rank values of one channel are 16 contiguous bytes of
+//    B ([d_out, r_cap] per adapter), and of one row of v.
+//  * Workgroups are remapped so that consecutive tiles land on the same XCD
+//    (the hardware deals workgroups round-robin over the 8 XCDs), and tiles
+//    are visited in groups of M tiles so each XCD's L2 holds the W0 panels it
+//    streams.
+#include "common.h"
+
+namespace lora {
+namespace {
+
+constexpr int kThreads = 256;
+
+enum FusedMode { kBF16 = 0, kW8A16 = 1, kW8A8 = 2 };
+
+struct FusedArgs {
+  const void* x;          // bf16 [T, ld_x] (kBF16, kW8A16) or e4m3 codes [T, ld_x] (kW8A8)
+  const void* W;          // bf16 [d_out, ld_w] or e4m3 codes
+  const float* w_scale;   // fp8 only
+  const float* s_x;       // kW8A8 only, per original row
+  const void* B;          // adapter pool B (bf16), or null
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  int32_t* seg;           // may be null (rows in batch order, no adapters)
+  const float* v;
+  void* y;
+  int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out;
+  int tiles_m, tiles_n, group_m;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+// XCD-aware, M-grouped tile order.  pid -> (tm, tn), a bijection.
+__device__ __forceinline__ void tile_of(int pid, int nblk, int tiles_m, int tiles_n, int group_m, int& tm,
+                                        int& tn) {
+  const int full = (nblk / 8) * 8;
+  int l = pid;
+  if (pid < full) l = (pid & 7) * (full / 8) + (pid >> 3);
+  const int per_group = group_m * tiles_n;
+  const int g = l / per_group;
+  const int first_m = g * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int in = l - g * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// fp8 e4m3 x16 (one 16-byte chunk) -> bf16 x16 (two 16-byte chunks), exact.
+__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4_t& c, u32x4_t& lo, u32x4_t& hi) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], true);
+    // e4m3 values carry 4 significant bits: the upper half of the fp32 is exact
+    const uint32_t w0 = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    const uint32_t w1 = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+    if (q < 2) { lo[2 * q] = w0; lo[2 * q + 1] = w1; }
+    else       { hi[2 * (q - 2)] = w0; hi[2 * (q - 2) + 1] = w1; }
+  }
+}
+
+template <int BM, int BN, int MODE>
+__global__ __launch_bounds__(kThreads) void fused_gemm_kernel(FusedArgs a) {
+  constexpr int WM = BM / 2, WN = BN / 2;         // wave tile
+  constexpr int TM = WM / 16, TN = WN / 16;       // 16x16 MFMA tiles per wave
+  constexpr int KB = MODE == kW8A8 ? 128 : 64;    // k elements per 128-byte row slab
+  constexpr int AR = BM / 32;                      // x rows staged per thread
+  constexpr int WR = MODE == kW8A16 ? BN / 64 : BN / 32;   // W rows staged per thread
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  SegPtrs P;
+  bool has_seg = a.seg != nullptr;
+  if (has_seg) {
+    P = seg_ptrs(a.seg, a.T);
+    has_seg = seg_valid(P, a.T);       // unusable buffer: batch order, base only
+  }
+
+  // ---- staging assignment --------------------------------------------
+  const uint8_t* arow[AR];
+  {
+    const int c = tid & 7, r = tid >> 3;
+#pragma unroll
+    for (int i = 0; i < AR; ++i) {
+      const int pos = m0 + r + 32 * i;
+      if (pos < a.T) {
+        const int row = has_seg ? P.perm[pos] : pos;
+        const size_t esz = MODE == kW8A8 ? 1 : 2;
+        arow[i] = static_cast<const uint8_t*>(a.x) + ((size_t)row * a.ld_x) * esz + c * 16;
+      } else {
+        arow[i] = nullptr;
+      }
+    }
+  }
+  const uint8_t* wrow[WR];
+  {
+    if constexpr (MODE == kW8A16) {
+      const int c = tid & 3, r = tid >> 2;
+#pragma unroll
+      for (int i = 0; i < WR; ++i) {
+        const int n = n0 + r + 64 * i;
+        wrow[i] = n < a.d_out ? static_cast<const uint8_t*>(a.W) + (size_t)n * a.ld_w + c * 16 : nullptr;
+      }
+    } else {
+      const int c = tid & 7, r = tid >> 3;
+      const size_t esz = MODE == kW8A8 ? 1 : 2;
+#pragma unroll
+      for (int i = 0; i < WR; ++i) {
+        const int n = n0 + r + 32 * i;
+        wrow[i] = n < a.d_out ? static_cast<const uint8_t*>(a.W) + ((size_t)n * a.ld_w) * esz + c * 16 : nullptr;
+      }
+    }
+  }
+
+  u32x4_t ra[AR];
+  u32x4_t rw[WR];
+  const u32x4_t zero4 = {0, 0, 0, 0};
+  const size_t kstep_bytes_x = MODE == kW8A8 ? 128 : 128;   // bytes of one row per k-step
+  const size_t kstep_bytes_w = MODE == kBF16 ? 128 : 64;     // fp8 widened: 64 codes = 64 bytes
+  // element offset of this thread's chunk inside a k-step, for the d_in bound
+  const int a_kofs = (tid & 7) * (MODE == kW8A8 ? 16 : 8);
+  const int w_kofs = MODE == kW8A16 ? (tid & 3) * 16 : (tid & 7) * (MODE == kW8A8 ? 16 : 8);
+
+  auto gload = [&](int kt) {
+    const int k0 = kt * KB;
+#pragma unroll
+    for (int i = 0; i < AR; ++i)
+      ra[i] = (arow[i] && k0 + a_kofs < a.d_in) ? ld128(arow[i] + (size_t)kt * kstep_bytes_x) : zero4;
+#pragma unroll
+    for (int i = 0; i < WR; ++i)
+      rw[i] = (wrow[i] && k0 + w_kofs < a.d_in) ? ld128(wrow[i] + (size_t)kt * kstep_bytes_w) : zero4;
+  };
+  auto lstore = [&](int buf) {
+    {
+      const int c = tid & 7, r = tid >> 3;
+#pragma unroll
+      for (int i = 0; i < AR; ++i) *reinterpret_cast<u32x4_t*>(&As[buf][swz(r + 32 * i, c)]) = ra[i];
+    }
+    if constexpr (MODE == kW8A16) {
+      const int c = tid & 3, r = tid >> 2;
+#pragma unroll
+      for (int i = 0; i < WR; ++i) {
+        u32x4_t lo, hi;
+        e4m3x16_to_bf16(rw[i], lo, hi);
+        *reinterpret_cast<u32x4_t*>(&Bs[buf][swz(r + 64 * i, 2 * c)]) = lo;
+        *reinterpret_cast<u32x4_t*>(&Bs[buf][swz(r + 64 * i, 2 * c + 1)]) = hi;
+      }
+    } else {
+      const int c = tid & 7, r = tid >> 3;
+#pragma unroll
+      for (int i = 0; i < WR; ++i) *reinterpret_cast<u32x4_t*>(&Bs[buf][swz(r + 32 * i, c)]) = rw[i];
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (a.d_in + KB - 1) / KB;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  const int frow = lane & 15, fk = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    if constexpr (MODE == kW8A8) {
+      // one K=128 MFMA per fragment pair; a lane's 32 codes are chunks 2*fk, 2*fk+1
+      i32x8_t fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WM + i * 16 + frow;
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(&As[buf][swz(row, 2 * fk)]);
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(&As[buf][swz(row, 2 * fk + 1)]);
+        fa[i] = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WN + j * 16 + frow;
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(&Bs[buf][swz(row, 2 * fk)]);
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(&Bs[buf][swz(row, 2 * fk + 1)]);
+        fb[j] = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * WM + i * 16 + frow;
+          fa[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&As[buf][swz(row, kk * 4 + fk)]));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = wn * WN + j * 16 + frow;
+          fb[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Bs[buf][swz(row, kk * 4 + fk)]));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ---------------------------------------------------------
+  const int row_base = m0 + wm * WM;          // first grouped position of this wave
+  const int col_base = n0 + wn * WN;
+  const int ocol = lane & 15, orow = (lane >> 4) * 4;
+
+  if constexpr (MODE != kBF16) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = col_base + j * 16 + ocol;
+      const float sw = n < a.d_out ? a.w_scale[n] : 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = sw;
+          if constexpr (MODE == kW8A8) {
+            const int pos = row_base + i * 16 + orow + e;
+            if (pos < a.T) s *= a.s_x[has_seg ? P.perm[pos] : pos];
+          }
+          acc[i][j][e] *= s;
+        }
+      }
+    }
+  }
+
+  if (has_seg && a.B != nullptr) {
+    const uint16_t* __restrict__ Bp = static_cast<const uint16_t*>(a.B);
+    const int n_active = P.sum[kNActive];
+    const int pend = min(row_base + WM, n_active);
+    int p = row_base;
+    while (p < pend) {
+      const int s = P.pos_seg[p];
+      const int ad = P.seg_adapter[s];
+      const int gend = min(P.seg_start[s + 1], pend);
+      const int r = a.slot_rank[ad];
+      const float sc = a.slot_scale[ad];
+      for (int kq = 0; kq * 32 < r; ++kq) {
+        const int k = kq * 32 + fk * 8;
+        bf16x8_t fb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = col_base + j * 16 + frow;
+          u32x4_t u = zero4;
+          if (n < a.d_out && k < r) {
+            u = ld128(Bp + ((size_t)ad * a.d_out + n) * a.r_cap + k);
+            if (k + 8 > r) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (k + 2 * e >= r) u[e] = 0;
+                else if (k + 2 * e + 1 >= r) u[e] &= 0xffffu;
+              }
+            }
+          }
+          fb[j] = __builtin_bit_cast(bf16x8_t, u);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int f0 = row_base + i * 16;
+          if (f0 + 16 <= p || f0 >= gend) continue;     // no row of this group here
+          const int pos = f0 + frow;
+          float vv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vv[e] = 0.f;
+          if (pos >= p && pos < gend) {
+            const float* vr = a.v + (size_t)pos * a.ld_v + k;
+            if (k < r) {
+              const u32x4_t c0 = ld128(vr);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vv[e] = __uint_as_float(c0[e]);
+            }
+            if (k + 4 < r) {
+              const u32x4_t c1 = ld128(vr + 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vv[4 + e] = __uint_as_float(c1[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = (k + e < r) ? vv[e] * sc : 0.f;
+          }
+          u32x4_t ua;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ua[e] = pack_bf16x2(vv[2 * e], vv[2 * e + 1]);
+          const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, ua);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+        }
+      }
+      p = gend;
+    }
+  }
+
+  uint16_t* __restrict__ Y = static_cast<uint16_t*>(a.y);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = row_base + i * 16 + orow + e;
+      if (pos >= a.T) continue;
+      const int row = has_seg ? P.perm[pos] : pos;
+      uint16_t* yr = Y + (size_t)row * a.ld_y;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = col_base + j * 16 + ocol;
+        if (n < a.d_out) yr[n] = f32_to_bf16(acc[i][j][e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (fp32 base, pool, x and y): LDS-tiled FMA GEMM, 64 x 64 tiles,
+// each thread 4 x 4 outputs; the adapter term is a per-element rank-r dot.
+// ---------------------------------------------------------------------------
+struct F32Args {
+  const float* x;
+  const float* W;
+  const float* B;
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  int32_t* seg;
+  const float* v;
+  float* y;
+  int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out, tiles_n;
+};
+
+__global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Ws[BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  bool has_seg = a.seg != nullptr;
+  SegPtrs P;
+  if (has_seg) {
+    P = seg_ptrs(a.seg, a.T);
+    has_seg = seg_valid(P, a.T);
+  }
+
+  const int lr = tid >> 2, lc = (tid & 3) * 4;    // staging: row, k offset
+  const int apos = m0 + lr;
+  const float* xrow = nullptr;
+  if (apos < a.T) xrow = a.x + (size_t)(has_seg ? P.perm[apos] : apos) * a.ld_x;
+  const float* wrow = (n0 + lr < a.d_out) ? a.W + (size_t)(n0 + lr) * a.ld_w : nullptr;
+
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < a.d_in; k0 += BK) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k0 + lc + e;
+      As[lc + e][lr] = (xrow && k < a.d_in) ? xrow[k] : 0.f;
+      Ws[lc + e][lr] = (wrow && k < a.d_in) ? wrow[k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float av[4], wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[j] = Ws[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], wv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  const int n_active = (has_seg && a.B) ? P.sum[kNActive] : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = m0 + ty * 4 + i;
+    if (pos >= a.T) continue;
+    const int row = has_seg ? P.perm[pos] : pos;
+    int ad = -1, r = 0;
+    float sc = 0.f;
+    if (pos < n_active) {
+      ad = P.seg_adapter[P.pos_seg[pos]];
+      r = a.slot_rank[ad];
+      sc = a.slot_scale[ad];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= a.d_out) continue;
+      float out = acc[i][j];
+      if (ad >= 0) {
+        const float* vr = a.v + (size_t)pos * a.ld_v;
+        const float* br = a.B + ((size_t)ad * a.d_out + n) * a.r_cap;
+        float d = 0.f;
+        for (int jj = 0; jj < r; ++jj) d = fmaf(vr[jj], br[jj], d);
+        out = fmaf(sc, d, out);
+      }
+      a.y[(size_t)row * a.ld_y + n] = out;
+    }
+  }
+}
+
+template <int BM, int BN, int MODE>
+hipError_t launch_cfg(FusedArgs a, hipStream_t st) {
+  a.tiles_m = (a.T + BM - 1) / BM;
+  a.tiles_n = (a.d_out + BN - 1) / BN;
+  a.group_m = a.tiles_m < 8 ? a.tiles_m : 8;
+  const int grid = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((fused_gemm_kernel<BM, BN, MODE>), dim3(grid), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const FusedArgs& a, hipStream_t st) {
+  const long big = (long)((a.T + 127) / 128) * ((a.d_out + 127) / 128);
+  if (big >= 512) return launch_cfg<128, 128, MODE>(a, st);
+  return launch_cfg<64, 64, MODE>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_t* seg, int T, const void* x,
+                        int ld_x, const float* v, int ld_v, void* y, int ld_y, int d_in, int d_out, int flags,
+                        void* workspace, hipStream_t st) {
+  if (T == 0 || d_out == 0) return hipSuccess;
+  if (base.dtype == LORA_F32) {
+    F32Args a;
+    a.x = static_cast<const float*>(x);
+    a.W = static_cast<const float*>(base.W);
+    a.B = pool ? static_cast<const float*>(pool->B) : nullptr;
+    a.slot_rank = pool ? pool->slot_rank : nullptr;
+    a.slot_scale = pool ? pool->slot_scale : nullptr;
+    a.seg = seg;
+    a.v = v;
+    a.y = static_cast<float*>(y);
+    a.r_cap = pool ? pool->r_cap : 0;
+    a.ld_v = ld_v;
+    a.ld_y = ld_y;
+    a.ld_x = ld_x;
+    a.ld_w = base.ld_w;
+    a.T = T;
+    a.d_in = d_in;
+    a.d_out = d_out;
+    a.tiles_n = (d_out + 63) / 64;
+    const int grid = ((T + 63) / 64) * a.tiles_n;
+    hipLaunchKernelGGL(fused_f32_kernel, dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  FusedArgs a;
+  a.x = x;
+  a.W = base.W;
+  a.w_scale = base.w_scale;
+  a.s_x = nullptr;
+  a.B = pool ? pool->B : nullptr;
+  a.slot_rank = pool ? pool->slot_rank : nullptr;
+  a.slot_scale = pool ? pool->slot_scale : nullptr;
+  a.seg = seg;
+  a.v = v;
+  a.y = y;
+  a.r_cap = pool ? pool->r_cap : 0;
+  a.ld_v = ld_v;
+  a.ld_y = ld_y;
+  a.ld_x = ld_x;
+  a.ld_w = base.ld_w;
+  a.T = T;
+  a.d_in = d_in;
+  a.d_out = d_out;
+  if (base.dtype == LORA_BF16) return launch_mode<kBF16>(a, st);
+  if (!(flags & LORA_FLAG_ACT_QUANT_E4M3)) return launch_mode<kW8A16>(a, st);
+  // W8A8: quantise x per token into the workspace, then the fp8 x fp8 product
+  uint8_t* q = static_cast<uint8_t*>(workspace);
+  const int ld_q = (d_in + 15) / 16 * 16;
+  float* s_x = reinterpret_cast<float*>(q + (size_t)T * ld_q);
+  hipError_t e = launch_quantize_e4m3(x, T, d_in, ld_x, q, ld_q, s_x, st);
+  if (e != hipSuccess) return e;
+  a.x = q;
+  a.ld_x = ld_q;
+  a.s_x = s_x;
+  return launch_mode<kW8A8>(a, st);
+}
+
+}  // namespace lora

@@ -1,0 +1,268 @@
+/*
+ * liblora -- batched heterogeneous-adapter ("multi-LoRA") linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * For a batch of T token rows, row i carrying adapter id a = ids[i]:
+ *
+ *     y_i = W0 x_i + [live_i] * s_a * B_a (A_a x_i)
+ *
+ * ("LLM-stack book 7.14 Multi-Tenant LoRA & Adapter Serving at Scale",
+ * 7.14.1: the parenthesised LoRA forward and the batched-heterogeneous
+ * problem; 7.14.2: stacked adapter pools indexed by a per-token id with -1
+ * meaning base only, segment pointers after grouping by adapter, SGMV/BGMV).
+ * A row is live when its id is >= 0 and its active flag is set; an inactive
+ * row stands for a released adapter and gets the base output only
+ * ("LoRazor", 3.2: released rows continue on the backbone-only path).
+ *
+ * The layer is split the way the pages split it ("LoRazor" 3.1.1 Eqs. 1-2;
+ * "LoRAForge" 2, Multi-LoRA Serving; "EpiLoRA" 3.1, kernels K1 and K2):
+ *   lora_build_segments / _dev   group the live rows by adapter (a1, a2)
+ *   lora_shrink                  v = A_a x          (rank-r down-projection)
+ *   lora_expand                  y += s_a B_a v     (unfused up-projection)
+ *   lora_fused_linear            y = W0 x (+ s_a B_a v in the epilogue),
+ *                                bf16 / fp32 / fp8-e4m3 base
+ *   lora_quantize_e4m3           per-token fp8 activation quantisation used
+ *                                by the fp8 W8A8 base product
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.  Every buffer is owned by the caller.  "device" pointers are HIP
+ *   device memory of the current device; "host" pointers are ordinary host
+ *   memory.  The library allocates nothing and keeps no device state.
+ * Streams.  Every call is asynchronous on the given hipStream_t (passed as
+ *   void*; NULL = the null stream).  No call synchronises the stream or reads
+ *   device memory back to the host.
+ * Errors.  Every call returns an int status (LORA_OK = 0).  All argument
+ *   checks run before any work is enqueued; a call that returns an error has
+ *   modified no output.  Device-side id validation (lora_build_segments_dev)
+ *   reports through the device summary instead (see there).
+ * Layouts.  Row-major throughout; ld_* are leading dimensions in elements.
+ *   Adapter pool of one projection:
+ *     A: [n_slots, r_cap, d_in]   row j of A_a is the j-th down direction
+ *     B: [n_slots, d_out, r_cap]  row n of B_a holds channel n's r_cap weights
+ *   Rank entries j >= slot_rank[a] are padding: never read by any kernel.
+ *   v (shrink output): fp32 [T, ld_v], row p = p-th row of the grouped order,
+ *     columns j < rank of that row's adapter; other entries are not written.
+ * Alignment.  x, A, B, W, y and v must be 16-byte aligned; d_in, d_out and
+ *   every ld must be multiples of 8 elements (16 for fp8 codes, 4 for fp32
+ *   v) so that rows can be moved in 128-bit loads.  Otherwise LORA_E_ALIGN.
+ */
+#ifndef LORA_H
+#define LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  LORA_OK = 0,
+  LORA_E_ARG = 1,    /* null pointer, negative size, ld < width, bad enum     */
+  LORA_E_ID = 2,     /* an adapter id < -1 or >= n_slots                      */
+  LORA_E_RANK = 3,   /* r_cap < 1 or r_cap > LORA_MAX_RANK                    */
+  LORA_E_DTYPE = 4,  /* unsupported dtype combination                         */
+  LORA_E_ALIGN = 5,  /* pointer or leading dimension not 16-byte aligned      */
+  LORA_E_HIP = 6,    /* a HIP launch or copy failed (see lora_last_error)     */
+  LORA_E_SIZE = 7    /* a size beyond a documented limit, or too small a
+                        workspace / segment buffer                            */
+};
+
+/* ---- element types --------------------------------------------------- */
+enum { LORA_F32 = 0, LORA_BF16 = 1, LORA_FP8_E4M3 = 2 };
+
+/* ---- limits ---------------------------------------------------------- */
+#define LORA_MAX_RANK 128          /* largest pool rank capacity r_cap        */
+#define LORA_DEV_MAX_SLOTS 8192    /* n_slots limit of lora_build_segments_dev */
+#define LORA_TILE_SMALL 16         /* row-tile height of the decode kernels   */
+#define LORA_TILE_LARGE 64         /* row-tile height of the prefill kernels  */
+
+/* ---- launch sizing (LoRazor 3.1) -------------------------------------- */
+enum {
+  /* grid = exactly the row tiles that hold live rows (sum_a ceil(m_a/BM))
+     times the column blocks; needs the host summary.                      */
+  LORA_LAUNCH_EXACT = 0,
+  /* fixed grid that strides over the device-side tile count; needs no host
+     summary, so the launch shape does not change from batch to batch.    */
+  LORA_LAUNCH_PERSISTENT = 1,
+  /* LoRazor's shared row bound (3.1.2, Eqs. 7-8): L = min(T, n_slots)
+     adapter slots x ceil(R/BM) row tiles, R from the host summary; blocks
+     without rows exit.                                                    */
+  LORA_LAUNCH_BUCKETED = 2,
+  /* the full-batch bound the pages start from (3.1.1): L x ceil(T/BM) row
+     tiles per launch, blocks without rows exit.  For comparison only.     */
+  LORA_LAUNCH_FULL_BATCH = 3
+};
+
+/* ---- fused-linear flags ---------------------------------------------- */
+#define LORA_FLAG_ACT_QUANT_E4M3 0x1  /* fp8 base: quantise x per token
+                                         (W8A8); default is W8A16           */
+
+/* Adapter pool of one projection (device pointers). */
+typedef struct {
+  const void* A;              /* [n_slots, r_cap, d_in], dtype               */
+  const void* B;              /* [n_slots, d_out, r_cap], dtype              */
+  const int32_t* slot_rank;   /* device int32 [n_slots], 0 <= rank <= r_cap  */
+  const float* slot_scale;    /* device fp32 [n_slots]: s_a = alpha/r (or any
+                                 caller-chosen scale; the kernels never see
+                                 alpha or r separately)                      */
+  int32_t dtype;              /* LORA_F32 or LORA_BF16                       */
+  int32_t n_slots;
+  int32_t r_cap;              /* 1 .. LORA_MAX_RANK                          */
+  int32_t d_in;
+  int32_t d_out;
+} lora_pool_t;
+
+/* Base weight of one projection (device pointers). */
+typedef struct {
+  const void* W;              /* [d_out, ld_w]: fp32 / bf16 values, or e4m3
+                                 codes (one byte each)                        */
+  const float* w_scale;       /* fp8 only: device fp32 [d_out], W0deq[n, k] =
+                                 e4m3(W[n, k]) * w_scale[n]; else NULL       */
+  int32_t dtype;              /* LORA_F32, LORA_BF16 or LORA_FP8_E4M3        */
+  int32_t ld_w;
+} lora_base_t;
+
+/* Host copy of a segment build's summary. */
+typedef struct {
+  int32_t n_active;     /* live rows                                         */
+  int32_t n_segments;   /* S = distinct adapters among live rows             */
+  int32_t m_max;        /* largest group                                     */
+  int32_t row_bound;    /* R = min{r in {16*2^k < T} U {T} : r >= m_max}
+                           (LoRazor 3.1.4, Eqs. 7-8); 0 if no live row       */
+  int32_t n_tiles_small;/* sum_a ceil(m_a / LORA_TILE_SMALL)                 */
+  int32_t n_tiles_large;/* sum_a ceil(m_a / LORA_TILE_LARGE)                 */
+  int32_t T;            /* rows the build covered                            */
+  int32_t error;        /* device builder only: LORA_E_ID if an id was out of
+                           range (outputs then undefined), else 0            */
+} lora_summary_t;
+
+/*
+ * Segment buffer.  One caller-allocated device buffer of
+ * lora_segment_words(T) int32 words (T = the row capacity), laid out as
+ *   [0, 16)                       summary words (lora_summary_t order)
+ *   perm        [T]               live rows grouped by adapter, then the
+ *                                 non-live rows in increasing order
+ *   pos_seg     [T]               segment index of each grouped position,
+ *                                 -1 for positions >= n_active
+ *   seg_start   [T + 1]           start of each segment in perm, plus the end
+ *   seg_adapter [T]               adapter id of each segment
+ *   tiles_small [2T]              (first position, segment) per 16-row tile
+ *   tiles_large [2T]              (first position, segment) per 64-row tile
+ * Only the first n_active / S / S+1 / n_tiles entries are meaningful.
+ */
+size_t lora_segment_words(int32_t T);
+
+/*
+ * Group token rows by adapter ("LLM-stack book" 7.14.2, the segment pointers
+ * seg_start / seg_adapter of the sorted batch; "LoRazor" 3.1.1, the
+ * adapter-grouped row-index array I_a with m_a = |I_a|).
+ *
+ *   ids      host int32 [T]: adapter id per row, -1 = no adapter
+ *   active   host uint8 [T] or NULL (NULL = every row with id >= 0 is live)
+ *   order    0: segments by ascending adapter id (canonical);
+ *            1: segments in order of first appearance in the batch
+ *            (the book's printed example).  Rows keep batch order inside a
+ *            segment in both cases.
+ *   staging  host int32 buffer of lora_segment_words(T) words, written by the
+ *            call and copied from asynchronously: it must stay untouched until
+ *            the stream has passed this call (pinned memory lets the copy run
+ *            asynchronously; pageable memory works but copies synchronously).
+ *   seg      device segment buffer of lora_segment_words(T) words.
+ *   summary  host: receives the summary immediately (before the copy lands),
+ *            so the next launches can be sized exactly on the host.
+ * Errors: LORA_E_ARG, LORA_E_ID (an id < -1 or >= n_slots; nothing copied).
+ */
+int lora_build_segments(const int32_t* ids, const uint8_t* active, int32_t T, int32_t n_slots,
+                        int32_t order, int32_t* staging, int32_t* seg, lora_summary_t* summary,
+                        void* stream);
+
+/* The same grouping computed on the host only, into a host buffer of
+ * lora_segment_words(T) words with the layout above; no HIP call. */
+int lora_plan_segments(const int32_t* ids, const uint8_t* active, int32_t T, int32_t n_slots,
+                       int32_t order, int32_t* plan, lora_summary_t* summary);
+
+/*
+ * Device variant: ids (device int32 [T]) and active (device uint8 [T] or
+ * NULL) are read on the GPU by one workgroup; the summary is written to the
+ * first words of `seg` only.  n_slots <= LORA_DEV_MAX_SLOTS.  An id out of
+ * range sets summary.error = LORA_E_ID on the device and leaves the other
+ * outputs undefined; kernels that consume such a segment buffer treat it as
+ * having no live rows.
+ */
+int lora_build_segments_dev(const int32_t* ids, const uint8_t* active, int32_t T, int32_t n_slots,
+                            int32_t order, int32_t* seg, void* stream);
+
+/*
+ * Shrink ("LoRazor" 3.1.1 Eq. 1; "LoRAForge" 5, rank-aware shrink):
+ *   v[p, j] = sum_k x[perm[p], k] * A_a[j, k]   for p < n_active, j < r_a,
+ * with a the adapter of p's segment, accumulated in fp32.
+ *   x      device [T, ld_x], pool dtype (fp32 or bf16)
+ *   v      device fp32 [T, ld_v], ld_v >= r_cap
+ *   summary  host summary of the segment build, or NULL when `launch` is
+ *            LORA_LAUNCH_PERSISTENT or LORA_LAUNCH_FULL_BATCH
+ * Decode-sized groups run a gather kernel (wave-wide dot products); groups of
+ * more than LORA_TILE_SMALL rows run an MFMA-tiled kernel.  Deterministic:
+ * fixed-order reductions, no atomics.
+ */
+int lora_shrink(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lora_summary_t* summary,
+                const void* x, int32_t ld_x, float* v, int32_t ld_v, int32_t launch, void* stream);
+
+/*
+ * Expand ("LoRazor" 3.1.1 Eq. 2; "LoRAForge" 5, RowExpand):
+ *   y[perm[p], n] += s_a * sum_{j < r_a} v[p, j] * B_a[n, j]   for p < n_active
+ * y is updated in place: fp32, or bf16 rounded once (nearest even) from
+ * fp32(y) + the fp32 update.  Rows that are not live are not touched.
+ */
+int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lora_summary_t* summary,
+                const float* v, int32_t ld_v, void* y, int32_t y_dtype, int32_t ld_y, int32_t launch,
+                void* stream);
+
+/*
+ * Fused linear ("EpiLoRA" 3.1 and Fig. 10, kernel K2: a GEMM over
+ * adapter-sorted rows whose epilogue applies the base scales and adds each
+ * adapter group's h B^T before writing the rows back in token order):
+ *   y[i, n] = epi( sum_k x[i, k] * W0[n, k] )
+ *   epi(acc) = acc * w_scale[n] [* s_x[i] for W8A8]
+ *              + [live_i] * s_a * sum_{j < r_a} v[p(i), j] * B_a[n, j]
+ * for every row i < T (p(i) = the grouped position of row i).
+ *   base     fp32 base with fp32 pool/x/y; bf16 base with bf16 pool/x/y;
+ *            fp8-e4m3 base with bf16 pool/x/y (W8A16: codes widened to bf16,
+ *            bf16 MFMA; W8A8 with LORA_FLAG_ACT_QUANT_E4M3: x quantised per
+ *            token into the workspace, fp8 MFMA).
+ *   pool, v  NULL, NULL for the base product alone (seg may then be NULL:
+ *            rows in batch order).
+ *   workspace / workspace_bytes: device scratch of at least
+ *            lora_fused_workspace_bytes(T, d_in, flags) bytes (0 unless W8A8).
+ * y must not alias x.  Each output element is written exactly once.
+ */
+int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
+                      const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,
+                      int32_t d_in, int32_t d_out, int32_t flags, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t flags);
+
+/*
+ * Per-token activation quantisation for the W8A8 base product ("EpiLoRA" 2
+ * and Fig. 4: x is quantised once per token, x -> (x_q, s_x)):
+ *   s_x[i] = amax_k |x[i, k]| / 448 in fp32 (1 for an all-zero row)
+ *   q[i, k] = e4m3( x[i, k] / s_x[i] ), fp32 division, round to nearest
+ *             even, saturating to +-448
+ *   x  device bf16 [T, ld_x]; q device uint8 [T, ld_q]; s_x device fp32 [T]
+ */
+int lora_quantize_e4m3(const void* x, int32_t T, int32_t d, int32_t ld_x, uint8_t* q, int32_t ld_q,
+                       float* s_x, void* stream);
+
+/* Static description of a status code. */
+const char* lora_status_string(int status);
+/* Text of the last LORA_E_HIP error on the calling thread ("" if none). */
+const char* lora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_H */

@@ -98,37 +98,38 @@ class Projection:
 
     # --- adapters --------------------------------------------------------
     def slot(self, a: int) -> Tuple[np.ndarray, np.ndarray]:
-        """Stored (A [r_cap, d_in], Bt [r_cap, d_out]) of slot ``a``.
+        """Stored (A [r_cap, d_in], B [d_out, r_cap]) of slot ``a``.
 
-        Rows j >= slot_rank[a] are zero.  Bt is B transposed (rank-major):
-        Bt[j, n] = B[n, j].  fp32 data -> float32 arrays, bf16 -> uint16 bits.
+        Rank entries j >= slot_rank[a] (rows of A, columns of B) are zero.
+        fp32 data -> float32 arrays, bf16 -> uint16 bits.  Draw order: A
+        row-major [r, d_in], then B row-major [d_out, r].
         """
         r = int(self.slot_rank[a])
         g = _rng(*self._key, _S_SLOT, a)
         if self.data_dtype == "fp32":
             A = np.zeros((self.r_cap, self.d_in), np.float32)
-            Bt = np.zeros((self.r_cap, self.d_out), np.float32)
+            B = np.zeros((self.d_out, self.r_cap), np.float32)
             A[:r] = g.standard_normal((r, self.d_in)) * self.a_std
-            Bt[:r] = g.standard_normal((r, self.d_out)) * self.b_std
-            return A, Bt
+            B[:, :r] = g.standard_normal((self.d_out, r)) * self.b_std
+            return A, B
         A = np.zeros((self.r_cap, self.d_in), np.uint16)
-        Bt = np.zeros((self.r_cap, self.d_out), np.uint16)
+        B = np.zeros((self.d_out, self.r_cap), np.uint16)
         A[:r] = bf16_round(g.standard_normal((r, self.d_in), dtype=np.float32) * np.float32(self.a_std))
-        Bt[:r] = bf16_round(g.standard_normal((r, self.d_out), dtype=np.float32) * np.float32(self.b_std))
-        return A, Bt
+        B[:, :r] = bf16_round(g.standard_normal((self.d_out, r), dtype=np.float32) * np.float32(self.b_std))
+        return A, B
 
     def pool(self, slots: Optional[List[int]] = None):
-        """Stacked (A_pool [N, r_cap, d_in], Bt_pool [N, r_cap, d_out]).
+        """Stacked (A_pool [N, r_cap, d_in], B_pool [N, d_out, r_cap]).
 
         Slots not listed in ``slots`` are left zero (callers that only need
         the adapters a batch touches pass that list).
         """
         dt = np.float32 if self.data_dtype == "fp32" else np.uint16
         A = np.zeros((self.n_slots, self.r_cap, self.d_in), dt)
-        Bt = np.zeros((self.n_slots, self.r_cap, self.d_out), dt)
+        B = np.zeros((self.n_slots, self.d_out, self.r_cap), dt)
         for a in (range(self.n_slots) if slots is None else slots):
-            A[a], Bt[a] = self.slot(a)
-        return A, Bt
+            A[a], B[a] = self.slot(a)
+        return A, B
 
 
 @dataclasses.dataclass

@@ -14,9 +14,10 @@ batched-heterogeneous problem"; LoRazor 3.1.1 Eqs. 1-2; LoRAForge 2
     v_i    = A_a[:r_a] x_i                        (shrink, rank-r_a down-projection)
     y_i    = base_i + [live_i] s_a B_a[:, :r_a] v_i   (expand, scaled and added)
 
-Storage convention used throughout: A_pool[a] is [R_cap, d_in] (row j is the
-j-th down-projection direction) and Bt_pool[a] is [R_cap, d_out] with
-Bt[j, n] = B[n, j].  Entries j >= r_a are padding and never read.
+Storage convention used throughout (the stacked-pool layout of the book's
+7.14.2 with one pool per projection): A_pool[a] is [R_cap, d_in] (row j is the
+j-th down-projection direction) and B_pool[a] is [d_out, R_cap].  Rank entries
+j >= r_a are padding and never read.
 
 Inputs arrive as *stored* values (float32 arrays, bf16 bit patterns, or e4m3
 codes with per-channel scales) and are decoded exactly to float64 here.
@@ -78,7 +79,7 @@ def shrink_rows(x, ids, active, A_pool, slot_rank) -> np.ndarray:
     return v
 
 
-def lora_delta(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale, v_rows=None) -> np.ndarray:
+def lora_delta(x, ids, active, A_pool, B_pool, slot_rank, slot_scale, v_rows=None) -> np.ndarray:
     """The adapter term s_a B_a v_i per row, grouped by adapter.
 
     One down- and one up-projection per distinct live adapter, each adapter's
@@ -89,7 +90,7 @@ def lora_delta(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale, v_rows=No
     ids = np.asarray(ids)
     live = live_rows(ids, active)
     T = X.shape[0]
-    d_out = np.asarray(Bt_pool).shape[2]
+    d_out = np.asarray(B_pool).shape[1]
     out = np.zeros((T, d_out), np.float64)
     for a in sorted(set(int(i) for i in ids[live])):
         rows = np.nonzero(live & (ids == a))[0]
@@ -98,11 +99,11 @@ def lora_delta(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale, v_rows=No
             v = X[rows] @ as_f64(A_pool[a][:r]).T
         else:
             v = np.asarray(v_rows, np.float64)[rows, :r]
-        out[rows] = float(slot_scale[a]) * (v @ as_f64(Bt_pool[a][:r]))
+        out[rows] = float(slot_scale[a]) * (v @ as_f64(B_pool[a][:, :r]).T)
     return out
 
 
-def lora_delta_per_row(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale,
+def lora_delta_per_row(x, ids, active, A_pool, B_pool, slot_rank, slot_scale,
                        rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Brute force, one row at a time: two matrix-vector products per row.
 
@@ -111,7 +112,7 @@ def lora_delta_per_row(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale,
     ids = np.asarray(ids)
     live = live_rows(ids, active)
     rows = range(X.shape[0]) if rows is None else rows
-    d_out = np.asarray(Bt_pool).shape[2]
+    d_out = np.asarray(B_pool).shape[1]
     out = np.zeros((len(rows), d_out), np.float64)
     for o, i in enumerate(rows):
         if not live[i]:
@@ -119,12 +120,12 @@ def lora_delta_per_row(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale,
         a = int(ids[i])
         r = int(slot_rank[a])
         A = as_f64(A_pool[a][:r])          # [r, d_in]
-        B = as_f64(Bt_pool[a][:r]).T       # [d_out, r]
+        B = as_f64(B_pool[a][:, :r])       # [d_out, r]
         out[o] = float(slot_scale[a]) * (B @ (A @ X[i]))
     return out
 
 
-def lora_delta_gathered(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale) -> np.ndarray:
+def lora_delta_gathered(x, ids, active, A_pool, B_pool, slot_rank, slot_scale) -> np.ndarray:
     """Gather-per-row formulation: every row gathers its own A, B, scale and
     rank mask, then two batched products (the book's toy MultiLoRALinear
     forward, which indexes the stacked pools by the per-token index)."""
@@ -134,26 +135,26 @@ def lora_delta_gathered(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale) 
     safe = np.where(live, ids, 0)
     R_cap = np.asarray(A_pool).shape[1]
     A = as_f64(np.asarray(A_pool)[safe])                 # [T, R_cap, d_in]
-    Bt = as_f64(np.asarray(Bt_pool)[safe])               # [T, R_cap, d_out]
+    B = as_f64(np.asarray(B_pool)[safe])                 # [T, d_out, R_cap]
     mask = (np.arange(R_cap)[None, :] < np.asarray(slot_rank)[safe][:, None]).astype(np.float64)
     s = np.asarray(slot_scale, np.float64)[safe] * live
     v = np.einsum("tk,tjk->tj", X, np.where(mask[:, :, None] > 0, A, 0.0)) * mask
-    d = np.einsum("tj,tjn->tn", v, np.where(mask[:, :, None] > 0, Bt, 0.0))
+    d = np.einsum("tj,tnj->tn", v, np.where(mask[:, None, :] > 0, B, 0.0))
     return d * s[:, None]
 
 
-def linear(x, w0, ids, active, A_pool, Bt_pool, slot_rank, slot_scale) -> np.ndarray:
+def linear(x, w0, ids, active, A_pool, B_pool, slot_rank, slot_scale) -> np.ndarray:
     """y = x W0^T + adapter term (fp64)."""
-    return base_output(x, w0) + lora_delta(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale)
+    return base_output(x, w0) + lora_delta(x, ids, active, A_pool, B_pool, slot_rank, slot_scale)
 
 
-def merged_linear(x, w0, A, Bt, r: int, s: float) -> np.ndarray:
+def merged_linear(x, w0, A, B, r: int, s: float) -> np.ndarray:
     """Single-adapter merged weight (W0 + s B A) applied to every row
     (the book's 7.14.1 "merging" paragraph): the multi-tenant result must equal
     this when every row carries the same adapter."""
     W = dequant_e4m3_rows(*w0) if isinstance(w0, tuple) else as_f64(w0)
     Af = as_f64(A)[:r]
-    Bf = as_f64(Bt)[:r].T
+    Bf = as_f64(B)[:, :r]
     return as_f64(x) @ (W + s * (Bf @ Af)).T
 
 
@@ -174,10 +175,10 @@ def act_quant_e4m3(x) -> tuple:
     return encode_e4m3(q), s
 
 
-def linear_w8a8(x, w0_codes, w0_scale, ids, active, A_pool, Bt_pool, slot_rank, slot_scale) -> np.ndarray:
+def linear_w8a8(x, w0_codes, w0_scale, ids, active, A_pool, B_pool, slot_rank, slot_scale) -> np.ndarray:
     """W8A8 variant: the base product uses the quantised activations,
     y_i = (x_q,i . W_q) s_x,i s_w + adapter term on the unquantised x."""
     codes, s_x = act_quant_e4m3(x)
     xq = decode_e4m3(codes) * s_x.astype(np.float64)[:, None]
     base = xq @ dequant_e4m3_rows(w0_codes, w0_scale).T
-    return base + lora_delta(x, ids, active, A_pool, Bt_pool, slot_rank, slot_scale)
+    return base + lora_delta(x, ids, active, A_pool, B_pool, slot_rank, slot_scale)

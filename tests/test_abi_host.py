@@ -1,0 +1,203 @@
+"""Host-side tests of the C-ABI library: it loads, exports every declared
+entry point, its host segment planner matches the oracle bit for bit, and
+argument validation rejects bad calls before anything is enqueued.
+
+No test here launches a kernel: every call with made-up device pointers is
+built to fail validation (asserted), so it is safe with or without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from golden_io import load
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+agm = pytest.importorskip("adapter_gemm_amd", reason="liblora.so not built")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lora.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(agm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(agm.EXPORTED) == names
+
+
+def test_status_strings():
+    for s in range(8):
+        assert agm.lib().lora_status_string(s)
+    assert agm.lib().lora_last_error() == b""
+
+
+def test_segment_words():
+    assert agm.segment_words(0) == 17
+    assert agm.segment_words(256) == 16 + 8 * 256 + 1
+
+
+def _split(plan, T):
+    h = agm.SEG_HEADER
+    perm = plan[h:h + T]
+    pos_seg = plan[h + T:h + 2 * T]
+    seg_start = plan[h + 2 * T:h + 3 * T + 1]
+    seg_adapter = plan[h + 3 * T + 1:h + 4 * T + 1]
+    ts = plan[h + 4 * T + 1:h + 6 * T + 1].reshape(-1, 2) if T else np.zeros((0, 2), np.int32)
+    tl = plan[h + 6 * T + 1:h + 8 * T + 1].reshape(-1, 2) if T else np.zeros((0, 2), np.int32)
+    return perm, pos_seg, seg_start, seg_adapter, ts, tl
+
+
+def _compare(ids, act, n_slots, order):
+    T = len(ids)
+    plan, s = agm.plan_segments(ids, act, n_slots, order)
+    ref = oracle.build_segments(ids, act, order)
+    perm, pos_seg, seg_start, seg_adapter, ts, tl = _split(plan, T)
+    S = ref["S"]
+    assert s["n_active"] == ref["n_active"] and s["n_segments"] == S and s["m_max"] == ref["m_max"]
+    assert s["T"] == T and s["error"] == 0
+    assert np.array_equal(perm, ref["perm"])
+    assert np.array_equal(seg_start[:S + 1], ref["seg_start"])
+    assert np.array_equal(seg_adapter[:S], ref["seg_adapter"])
+    # segment index of every grouped position
+    want_pos = np.full(T, -1)
+    for k in range(S):
+        want_pos[ref["seg_start"][k]:ref["seg_start"][k + 1]] = k
+    assert np.array_equal(pos_seg, want_pos)
+    for tile, lst, n in ((agm.TILE_SMALL, ts, s["n_tiles_small"]), (agm.TILE_LARGE, tl, s["n_tiles_large"])):
+        want = oracle.row_tiles(ref["seg_start"], tile)
+        assert n == len(want)
+        assert [(int(b), int(a)) for a, b in lst[:n]] == [(w[0], w[1]) for w in want]
+    want_R = oracle.row_bound(T, ref["m_max"]) if ref["n_active"] else 0
+    assert s["row_bound"] == want_R
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("order", [0, 1])
+def test_host_planner_matches_oracle(seed, order):
+    g = np.random.default_rng(100 + seed)
+    T = int(g.integers(0, 700))
+    N = int(g.integers(1, 300))
+    ids = g.integers(-1, N, T).astype(np.int32)
+    act = (g.uniform(size=T) > 0.3).astype(np.uint8) if seed % 2 else None
+    _compare(ids, act, N, order)
+
+
+def test_host_planner_workloads():
+    from lora_inputs import make_workload, CONFIG_NAMES
+    for name in CONFIG_NAMES:
+        w = make_workload(name)
+        _compare(w.ids, w.active, w.projections[0].n_slots, 0)
+
+
+def test_host_planner_book_example():
+    g = load("segments_book_example.txt")
+    ids = g["ids"].astype(np.int32)
+    plan, s = agm.plan_segments(ids, None, 8, 1)
+    _, _, seg_start, seg_adapter, _, _ = _split(plan, len(ids))
+    assert list(seg_start[:3]) == list(g["printed_seg_start"].astype(int))
+    assert list(seg_adapter[:3]) == list(g["printed_seg_adapter"].astype(int))
+
+
+def test_planner_errors():
+    with pytest.raises(agm.LoraError) as e:
+        agm.plan_segments(np.array([0, 5], np.int32), None, 5, 0)
+    assert e.value.status == agm.LORA_E_ID
+    with pytest.raises(agm.LoraError) as e:
+        agm.plan_segments(np.array([0, -2], np.int32), None, 5, 0)
+    assert e.value.status == agm.LORA_E_ID
+    with pytest.raises(agm.LoraError) as e:
+        agm.plan_segments(np.array([0], np.int32), None, 5, 2)
+    assert e.value.status == agm.LORA_E_ARG
+
+
+# ---- validation with made-up device addresses (never reach a launch) ---------
+
+FAKE = 1 << 40           # 16-byte aligned, never dereferenced
+
+
+def _pool(**over):
+    d = dict(A=FAKE, B=FAKE, slot_rank=FAKE, slot_scale=FAKE, dtype=agm.BF16, n_slots=4, r_cap=16,
+             d_in=64, d_out=64)
+    d.update(over)
+    return agm.PoolDesc(**d)
+
+
+def _shrink(pool, seg=FAKE, T=4, x=FAKE, ld_x=64, v=FAKE, ld_v=16, launch=agm.LAUNCH_PERSISTENT):
+    return agm.lib().lora_shrink(None if pool is None else ctypes.byref(pool), seg, T, None, x, ld_x, v, ld_v,
+                                 launch, None)
+
+
+def test_shrink_validation():
+    L = agm
+    assert _shrink(None) == L.LORA_E_ARG
+    assert _shrink(_pool(A=None)) == L.LORA_E_ARG
+    assert _shrink(_pool(r_cap=0)) == L.LORA_E_RANK
+    assert _shrink(_pool(r_cap=136)) == L.LORA_E_RANK
+    assert _shrink(_pool(r_cap=12)) == L.LORA_E_ALIGN          # bf16 rank rows need 16-byte multiples
+    assert _shrink(_pool(dtype=7)) == L.LORA_E_DTYPE
+    assert _shrink(_pool(d_in=60)) == L.LORA_E_ALIGN
+    assert _shrink(_pool(A=FAKE + 8)) == L.LORA_E_ALIGN
+    assert _shrink(_pool(), seg=None) == L.LORA_E_ARG
+    assert _shrink(_pool(), T=-1) == L.LORA_E_ARG
+    assert _shrink(_pool(), ld_x=32) == L.LORA_E_ARG
+    assert _shrink(_pool(), ld_v=8) == L.LORA_E_ARG
+    assert _shrink(_pool(), x=FAKE + 4) == L.LORA_E_ALIGN
+    assert _shrink(_pool(), launch=9) == L.LORA_E_ARG
+    assert _shrink(_pool(), launch=agm.LAUNCH_EXACT) == L.LORA_E_ARG    # EXACT needs the host summary
+
+
+def test_expand_validation():
+    lib = agm.lib()
+    p = _pool()
+    e = lambda **k: lib.lora_expand(ctypes.byref(k.get("pool", p)), k.get("seg", FAKE), 4, None,
+                                    k.get("v", FAKE), 16, k.get("y", FAKE), k.get("yd", agm.BF16),
+                                    k.get("ld_y", 64), agm.LAUNCH_PERSISTENT, None)
+    assert e(yd=agm.FP8_E4M3) == agm.LORA_E_DTYPE
+    assert e(ld_y=32) == agm.LORA_E_ARG
+    assert e(y=FAKE + 2) == agm.LORA_E_ALIGN
+    assert e(v=None) == agm.LORA_E_ARG
+    assert e(pool=_pool(B=None)) == agm.LORA_E_ARG
+
+
+def test_fused_validation():
+    lib = agm.lib()
+    base = agm.BaseDesc(FAKE, None, agm.BF16, 64)
+
+    def f(base=base, pool=None, seg=None, v=None, flags=0, ws=None, ws_bytes=0, x=FAKE, y=FAKE + 4096,
+          d_in=64, d_out=64):
+        return lib.lora_fused_linear(ctypes.byref(base), None if pool is None else ctypes.byref(pool), seg, 4,
+                                     x, 64, v, 16, y, 64, d_in, d_out, flags, ws, ws_bytes, None)
+
+    assert f(flags=0x10) == agm.LORA_E_ARG
+    assert f(flags=agm.FLAG_ACT_QUANT_E4M3) == agm.LORA_E_DTYPE          # W8A8 needs an fp8 base
+    assert f(base=agm.BaseDesc(FAKE, None, agm.FP8_E4M3, 64)) == agm.LORA_E_ARG   # no w_scale
+    assert f(base=agm.BaseDesc(FAKE, FAKE, agm.FP8_E4M3, 64), flags=agm.FLAG_ACT_QUANT_E4M3) == agm.LORA_E_SIZE
+    assert f(base=agm.BaseDesc(FAKE, FAKE, agm.FP8_E4M3, 64), d_in=56) == agm.LORA_E_ALIGN
+    assert f(pool=_pool(dtype=agm.F32), seg=FAKE, v=FAKE) == agm.LORA_E_DTYPE
+    assert f(pool=_pool(), seg=None, v=FAKE) == agm.LORA_E_ARG
+    assert f(pool=_pool(d_out=128), seg=FAKE, v=FAKE) == agm.LORA_E_ARG
+    assert f(v=FAKE) == agm.LORA_E_ARG                                    # v without a pool
+    assert f(x=FAKE, y=FAKE) == agm.LORA_E_ARG                            # y aliases x
+    assert f(d_out=60) == agm.LORA_E_ALIGN
+    assert f(base=agm.BaseDesc(None, None, agm.BF16, 64)) == agm.LORA_E_ARG
+
+
+def test_quant_and_dev_builder_validation():
+    lib = agm.lib()
+    assert lib.lora_quantize_e4m3(FAKE, 4, 24, 32, FAKE, 32, FAKE, None) == agm.LORA_E_ALIGN
+    assert lib.lora_quantize_e4m3(FAKE, 4, 32, 16, FAKE, 32, FAKE, None) == agm.LORA_E_ARG
+    assert lib.lora_build_segments_dev(FAKE, None, 8, agm.DEV_MAX_SLOTS + 1, 0, FAKE, None) == agm.LORA_E_SIZE
+    assert lib.lora_build_segments_dev(FAKE, None, 8, 4, 3, FAKE, None) == agm.LORA_E_ARG
+    assert lib.lora_build_segments_dev(None, None, 8, 4, 0, FAKE, None) == agm.LORA_E_ARG
+    assert lib.lora_fused_workspace_bytes(4, 64, 0) == 0
+    assert lib.lora_fused_workspace_bytes(4, 64, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16

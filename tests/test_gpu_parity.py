@@ -1,0 +1,327 @@
+"""GPU parity: every library call against the fp64 oracle on the same seeded
+inputs, through the C-ABI.
+
+Tolerances (relative L2 against the oracle):
+  segments                 bit-exact
+  fp32 outputs (v, fp32 y) 1e-4
+  bf16 outputs             1e-2
+  fp8-base outputs         3e-2 (oracle on the dequantised weights)
+Each output is checked globally, per row (max over rows) and on the adapter
+term alone (expand on a zero y, or the fused call on a zero base).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():      # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import adapter_gemm_amd as agm
+import oracle
+from lora_inputs import make_workload
+from gpu_helpers import (DEV, DevProjection, segments, split_seg, rel_l2, row_rel_l2, to_f64, bf16_dev)
+
+TOL = {"fp32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
+
+# small variants: several tiles in every dimension and ragged tails
+# (T, d_in, d_out not multiples of the tile sizes)
+SMALL = {
+    "tiny_sgmv": dict(),
+    "decode_bgmv": dict(T=300, d_in=1032, d_out=1048, n_slots=40),
+    "prefill_sgmv": dict(T=1000, d_in=520, d_out=1176, n_slots=24, n_req=7),
+    "fp8_fused": dict(T=200, d_in=1040, d_out=904, n_slots=32, r=64),
+    "llama_layer": dict(n_slots=96, n_req=3, prefill_len=40, n_decode=70,
+                        shapes=[("q", 520, 264), ("down", 264, 520)]),
+}
+
+
+def _tol(p):
+    return TOL["fp8"] if p.base_dtype == "fp8" else TOL[p.data_dtype]
+
+
+def _v_ref(dp, w, segd):
+    """oracle v in grouped order [n_active, r_cap]"""
+    v_rows = oracle.shrink_rows(dp.x_host, w.ids, w.active, dp.A_host, dp.p.slot_rank)
+    n = int(segd["sum"][0])
+    return v_rows[segd["perm"][:n]]
+
+
+# ---- a1: segments ------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("device_build", [False, True])
+def test_segments_bit_exact(name, order, device_build):
+    w = make_workload(name, **SMALL[name])
+    N = w.projections[0].n_slots
+    seg, s = segments(w, N, order, device_build)
+    d = split_seg(seg, w.T)
+    ref = oracle.build_segments(w.ids, w.active, order)
+    S = ref["S"]
+    assert s.error == 0 and s.n_active == ref["n_active"] and s.n_segments == S and s.m_max == ref["m_max"]
+    assert np.array_equal(d["perm"], ref["perm"])
+    assert np.array_equal(d["seg_start"][:S + 1], ref["seg_start"])
+    assert np.array_equal(d["seg_adapter"][:S], ref["seg_adapter"])
+    want_pos = np.full(w.T, -1)
+    for k in range(S):
+        want_pos[ref["seg_start"][k]:ref["seg_start"][k + 1]] = k
+    assert np.array_equal(d["pos_seg"], want_pos)
+    for key, tile, n in (("tiles_small", 16, s.n_tiles_small), ("tiles_large", 64, s.n_tiles_large)):
+        want = oracle.row_tiles(ref["seg_start"], tile)
+        assert n == len(want)
+        assert [(int(b), int(a)) for a, b in d[key][:n]] == [(x[0], x[1]) for x in want]
+    assert s.row_bound == (oracle.row_bound(w.T, ref["m_max"]) if ref["n_active"] else 0)
+
+
+def test_device_segments_large_and_bad_ids():
+    g = np.random.default_rng(5)
+    for T, N in [(1, 1), (1023, 7), (1025, 8192), (5000, 300), (20000, 1024)]:
+        ids = g.integers(-1, N, T).astype(np.int32)
+        act = (g.uniform(size=T) > 0.2).astype(np.uint8)
+        w = type("W", (), {})()
+        w.ids, w.active, w.T = ids, act, T
+        seg, s = segments(w, N, 0, True)
+        d = split_seg(seg, T)
+        ref = oracle.build_segments(ids, act, 0)
+        assert np.array_equal(d["perm"], ref["perm"]), (T, N)
+        assert s.n_tiles_small == len(oracle.row_tiles(ref["seg_start"], 16))
+    # an out-of-range id is reported on the device; kernels then see no rows
+    w.ids = np.array([0, 3, 9], np.int32)
+    w.active = np.ones(3, np.uint8)
+    w.T = 3
+    seg, s = segments(w, 4, 0, True)
+    assert s.error == agm.LORA_E_ID
+
+
+# ---- a3 shrink, a4 expand ----------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_shrink_expand_parity(name):
+    w = make_workload(name, **SMALL[name])
+    for p in w.projections:
+        dp = DevProjection(w, p)
+        seg, s = segments(w, p.n_slots)
+        segd = split_seg(seg, w.T)
+        v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+        agm.shrink(dp.pool, seg, w.T, s, dp.x, v)
+        # adapter term alone: expand on y = 0
+        y = torch.zeros(w.T, p.d_out, dtype=dp.ydtype, device=DEV)
+        agm.expand(dp.pool, seg, w.T, s, v, y)
+        torch.cuda.synchronize()
+        n = s.n_active
+        vg = v.cpu().numpy().astype(np.float64)[:n]
+        vr = _v_ref(dp, w, segd)
+        mask = np.arange(p.r_cap)[None, :] < p.slot_rank[w.ids[segd["perm"][:n]]][:, None]
+        assert rel_l2(np.where(mask, vg, 0), vr) <= TOL["fp32"], name
+        d_ref = oracle.lora_delta(*dp.oracle_args(w))
+        d_got = to_f64(y)
+        live = oracle.live_rows(w.ids, w.active)
+        tol = _tol(p)
+        assert rel_l2(d_got, d_ref) <= tol
+        assert row_rel_l2(d_got[live], d_ref[live]) <= tol
+        assert np.all(d_got[~live] == 0)                 # rows not live untouched
+
+
+@pytest.mark.parametrize("launch", [agm.LAUNCH_EXACT, agm.LAUNCH_PERSISTENT, agm.LAUNCH_BUCKETED,
+                                    agm.LAUNCH_FULL_BATCH])
+def test_launch_modes_bitwise_identical(launch):
+    w = make_workload("llama_layer", **SMALL["llama_layer"])
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, p.n_slots)
+    outs = []
+    for mode in (agm.LAUNCH_EXACT, launch):
+        v = torch.zeros(w.T, p.r_cap, device=DEV)
+        y = bf16_dev(w.x(p)[:, :p.d_out].copy()) if p.d_out <= p.d_in else torch.zeros(w.T, p.d_out,
+                                                                                          dtype=torch.bfloat16,
+                                                                                          device=DEV)
+        agm.shrink(dp.pool, seg, w.T, s, dp.x, v, launch=mode)
+        agm.expand(dp.pool, seg, w.T, s, v, y, launch=mode)
+        torch.cuda.synchronize()
+        outs.append((v.cpu(), y.cpu()))
+    n = s.n_active
+    assert torch.equal(outs[0][0][:n], outs[1][0][:n])
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
+def test_expand_leaves_other_rows_bitwise_untouched():
+    w = make_workload("decode_bgmv", **SMALL["decode_bgmv"])
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, p.n_slots)
+    v = torch.zeros(w.T, p.r_cap, device=DEV)
+    agm.shrink(dp.pool, seg, w.T, s, dp.x, v)
+    y0 = torch.randn(w.T, p.d_out, device=DEV).to(torch.bfloat16)
+    y = y0.clone()
+    agm.expand(dp.pool, seg, w.T, s, v, y)
+    torch.cuda.synchronize()
+    dead = torch.from_numpy(~oracle.live_rows(w.ids, w.active)).to(DEV)
+    assert dead.sum() > 0
+    assert torch.equal(y[dead].view(torch.int16), y0[dead].view(torch.int16))
+    # and the live rows changed consistently with base + delta
+    ref = y0.double().cpu().numpy() + oracle.lora_delta(*dp.oracle_args(w))
+    assert rel_l2(to_f64(y), ref) <= TOL["bf16"]
+
+
+# ---- a5 fused linear ----------------------------------------------------------------
+
+def _fused(dp, seg, s, w, flags=0, zero_base=False, with_pool=True):
+    p = dp.p
+    v = torch.zeros(w.T, p.r_cap, device=DEV)
+    if with_pool:
+        agm.shrink(dp.pool, seg, w.T, s, dp.x, v)
+    base = dp.base
+    if zero_base:
+        Wz = torch.zeros_like(dp.W)
+        base = agm.base_desc(Wz, dp.w_scale)
+    y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(dp.ydtype)
+    ws = None
+    if flags:
+        ws = torch.empty(agm.fused_workspace_bytes(w.T, p.d_in, flags), dtype=torch.uint8, device=DEV)
+    agm.fused_linear(base, dp.pool if with_pool else None, seg if with_pool else None, dp.x,
+                     v if with_pool else None, y, flags=flags, workspace=ws)
+    torch.cuda.synchronize()
+    return to_f64(y)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_parity(name):
+    w = make_workload(name, **SMALL[name])
+    for p in w.projections:
+        dp = DevProjection(w, p)
+        seg, s = segments(w, p.n_slots)
+        y = _fused(dp, seg, s, w)
+        ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+        tol = _tol(p)
+        assert np.isfinite(y).all()
+        assert rel_l2(y, ref) <= tol, (name, p.name, rel_l2(y, ref))
+        assert row_rel_l2(y, ref) <= tol
+        # adapter term alone (zero base)
+        d = _fused(dp, seg, s, w, zero_base=True)
+        d_ref = oracle.lora_delta(*dp.oracle_args(w))
+        live = oracle.live_rows(w.ids, w.active)
+        if live.any():
+            assert rel_l2(d, d_ref) <= tol
+            assert row_rel_l2(d[live], d_ref[live]) <= tol
+        # inactive rows equal the base-only run bit for bit
+        yb = _fused(dp, seg, s, w, with_pool=False)
+        assert np.array_equal(y[~live], yb[~live])
+
+
+def test_fused_w8a8_parity():
+    w = make_workload("fp8_fused", **SMALL["fp8_fused"])
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, p.n_slots)
+    y = _fused(dp, seg, s, w, flags=agm.FLAG_ACT_QUANT_E4M3)
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    assert rel_l2(y, ref) <= TOL["fp8"]
+    assert row_rel_l2(y, ref) <= TOL["fp8"]
+    # same quantised activations as the oracle's W8A8 definition: much closer
+    ref8 = oracle.linear_w8a8(dp.x_host, dp.w0_host[0], dp.w0_host[1], *dp.oracle_args(w)[1:])
+    assert rel_l2(y, ref8) <= TOL["bf16"]
+
+
+def test_quantize_e4m3_bit_exact():
+    g = np.random.default_rng(0)
+    from lora_inputs import bf16_round
+    x = bf16_round((g.standard_normal((37, 1040)) * np.exp(g.uniform(-6, 6, (37, 1)))).astype(np.float32))
+    x[5] = 0
+    xd = bf16_dev(x)
+    q = torch.empty(37, 1040, dtype=torch.uint8, device=DEV)
+    s = torch.empty(37, dtype=torch.float32, device=DEV)
+    agm.quantize_e4m3(xd, q, s)
+    torch.cuda.synchronize()
+    codes, sx = oracle.act_quant_e4m3(x)
+    assert np.array_equal(s.cpu().numpy(), sx)
+    assert np.array_equal(q.cpu().numpy(), codes)
+
+
+def test_order_and_determinism():
+    w = make_workload("decode_bgmv", **SMALL["decode_bgmv"])
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg0, s0 = segments(w, p.n_slots, 0)
+    seg1, s1 = segments(w, p.n_slots, 1)
+    ya = _fused(dp, seg0, s0, w)
+    yb = _fused(dp, seg0, s0, w)
+    yc = _fused(dp, seg1, s1, w)
+    assert np.array_equal(ya, yb)                    # bitwise reproducible
+    assert rel_l2(yc, ya) <= 1e-3                    # segment order does not matter
+
+
+# ---- edge cases ------------------------------------------------------------------
+
+def _custom(T, d_in, d_out, N, r_cap, ranks, ids, active=None, dtype="bf16", seed=0):
+    """A workload built from explicit ids/ranks with the generator's draws."""
+    from lora_inputs import Projection, Workload
+    key = (seed, 99)
+    p = Projection("p", d_in, d_out, N, r_cap, np.asarray(ranks, np.int32),
+                   np.linspace(0.5, 2.0, N).astype(np.float32), 0.05, 0.05, 0.05, dtype, dtype, key)
+    act = np.ones(T, np.uint8) if active is None else np.asarray(active, np.uint8)
+    return Workload("custom", seed, T, [p], np.asarray(ids, np.int32), act, dtype)
+
+
+@pytest.mark.parametrize("ranks,r_cap", [([1, 2, 4, 12], 16), ([16, 31, 32, 7], 32), ([64, 1, 33, 64], 64),
+                                         ([128, 100, 5, 1], 128)])
+def test_rank_edge_cases(ranks, r_cap):
+    g = np.random.default_rng(len(ranks) + r_cap)
+    T = 77
+    ids = g.integers(-1, 4, T)
+    w = _custom(T, 264, 200, 4, r_cap, ranks, ids)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, 4)
+    y = _fused(dp, seg, s, w)
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    assert rel_l2(y, ref) <= TOL["bf16"] and row_rel_l2(y, ref) <= TOL["bf16"]
+    v = torch.zeros(T, r_cap, device=DEV)
+    agm.shrink(dp.pool, seg, T, s, dp.x, v)
+    yz = torch.zeros(T, p.d_out, dtype=torch.bfloat16, device=DEV)
+    agm.expand(dp.pool, seg, T, s, v, yz)
+    torch.cuda.synchronize()
+    d_ref = oracle.lora_delta(*dp.oracle_args(w))
+    assert rel_l2(to_f64(yz), d_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", ["empty", "all_none", "all_inactive", "one_row", "one_adapter_big"])
+def test_degenerate_batches(case):
+    T = {"empty": 0, "one_row": 1}.get(case, 130)
+    ids = np.zeros(T, np.int32)
+    act = np.ones(T, np.uint8)
+    if case == "all_none":
+        ids[:] = -1
+    if case == "all_inactive":
+        act[:] = 0
+    w = _custom(T, 136, 72, 3, 16, [16, 8, 4], ids, act)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, 3)
+    y = _fused(dp, seg, s, w) if T else None
+    if T:
+        ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+        assert rel_l2(y, ref) <= TOL["bf16"]
+    for mode in (agm.LAUNCH_EXACT, agm.LAUNCH_PERSISTENT, agm.LAUNCH_BUCKETED, agm.LAUNCH_FULL_BATCH):
+        v = torch.zeros(max(T, 1), 16, device=DEV)
+        yz = torch.zeros(max(T, 1), 72, dtype=torch.bfloat16, device=DEV)
+        agm.shrink(dp.pool, seg, T, s, dp.x if T else yz, v[:T] if T else v, launch=mode)
+        agm.expand(dp.pool, seg, T, s, v, yz, launch=mode)
+        torch.cuda.synchronize()
+        if T:
+            d_ref = oracle.lora_delta(*dp.oracle_args(w))
+            assert rel_l2(to_f64(yz)[:T], d_ref) <= TOL["bf16"]
+
+
+def test_zero_B_gives_base_exactly():
+    g = np.random.default_rng(3)
+    T = 90
+    w = _custom(T, 256, 136, 5, 16, [16] * 5, g.integers(-1, 5, T))
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    dp.B.zero_()
+    seg, s = segments(w, 5)
+    y = _fused(dp, seg, s, w)
+    yb = _fused(dp, seg, s, w, with_pool=False)
+    assert np.array_equal(y, yb)

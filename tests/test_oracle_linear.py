@@ -23,12 +23,12 @@ from golden_io import load
 def _hand():
     g = load("hand_example.txt")
     A = np.full((2, 2, 3), np.nan)
-    Bt = np.full((2, 2, 2), np.nan)
+    B = np.full((2, 2, 2), np.nan)       # [slot, d_out, R_cap]
     A[0, :1] = g["A0"]
     A[1, :2] = g["A1"]
-    Bt[0, :1] = np.asarray(g["B0"]).reshape(2, 1).T
-    Bt[1, :2] = np.asarray(g["B1"]).T
-    return g, A, Bt
+    B[0, :, :1] = np.asarray(g["B0"]).reshape(2, 1)
+    B[1, :, :2] = np.asarray(g["B1"])
+    return g, A, B
 
 
 def test_hand_example():
@@ -54,10 +54,10 @@ def _case(T=37, d_in=24, d_out=20, N=5, R_cap=6, seed=0, pad=np.nan):
     rank = g.integers(1, R_cap + 1, N)
     scale = g.uniform(0.25, 3, N)
     A = np.full((N, R_cap, d_in), pad)
-    Bt = np.full((N, R_cap, d_out), pad)
+    Bt = np.full((N, d_out, R_cap), pad)
     for a in range(N):
         A[a, :rank[a]] = g.standard_normal((rank[a], d_in))
-        Bt[a, :rank[a]] = g.standard_normal((rank[a], d_out))
+        Bt[a, :, :rank[a]] = g.standard_normal((d_out, rank[a]))
     ids = g.integers(-1, N, T)
     act = (g.uniform(size=T) > 0.2).astype(np.uint8)
     return x, W0, ids, act, A, Bt, rank, scale
@@ -93,7 +93,7 @@ def test_selector_closed_form():
     x = g.integers(-8, 8, (T, d_in)).astype(np.float64)
     W0 = np.zeros((d_out, d_in))
     A = np.full((N, R, d_in), np.nan)
-    Bt = np.full((N, R, d_out), np.nan)
+    Bt = np.full((N, d_out, R), np.nan)
     rank = np.array([1, 3, 4])
     scale = np.array([2.0, -0.5, 3.0])
     picks = {}
@@ -101,7 +101,7 @@ def test_selector_closed_form():
         ks = g.choice(d_in, rank[a], replace=False)
         ns = g.choice(d_out, rank[a], replace=False)
         A[a, :rank[a]] = np.eye(d_in)[ks]
-        Bt[a, :rank[a]] = np.eye(d_out)[ns]
+        Bt[a, :, :rank[a]] = np.eye(d_out)[ns].T
         picks[a] = (ks, ns)
     ids = np.array([0, 1, 2, -1, 2, 1, 0, 2])
     y = L.linear(x, W0, ids, None, A, Bt, rank, scale)
@@ -152,7 +152,7 @@ def _brute(x, W0, ids, act, A, Bt, rank, scale):
                     vj = 0.0
                     for k in range(d_in):
                         vj += float(A[a][j][k]) * float(x[i][k])
-                    acc += float(scale[a]) * float(Bt[a][j][n]) * vj
+                    acc += float(scale[a]) * float(Bt[a][n][j]) * vj
             y[i][n] = acc
     return np.array(y)
 
@@ -170,7 +170,7 @@ def test_padding_rows_never_read():
     A2, B2 = A.copy(), Bt.copy()
     for a in range(A.shape[0]):
         A2[a, rank[a]:] = np.nan
-        B2[a, rank[a]:] = np.nan
+        B2[a, :, rank[a]:] = np.nan
     y1 = L.linear(x, W0, ids, act, A2, B2, rank, scale)
     assert np.array_equal(y0, y1)
 
@@ -218,8 +218,8 @@ def _mutants():
 
     def swapped_pools(x, W0, ids, act, A, Bt, rank, scale):
         # uses B^T's first d_in columns as the down-projection (square-ish mix-up)
-        d_in = np.asarray(x).shape[1]
-        A2 = np.asarray(Bt)[:, :, :d_in] if np.asarray(Bt).shape[2] >= d_in else A
+        # B's rank columns read as if they were A's rank rows (square shapes)
+        A2 = np.swapaxes(np.asarray(Bt), 1, 2) if np.asarray(Bt).shape[1] == np.asarray(x).shape[1] else A
         return good(x, W0, ids, act, A2, Bt, rank, scale)
 
     return [no_scale, wrong_sign, transposed_base, rank_minus_one, rank_plus_one,
