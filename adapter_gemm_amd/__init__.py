@@ -60,6 +60,10 @@ class Summary(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime (same soname as ROCm's); loading torch
+    # first makes liblora bind to that one copy instead of opening a second
+    # runtime in the same process.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m adapter_gemm_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
@@ -98,6 +102,11 @@ def _check(status: int, where: str):
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _ld(t) -> int:
+    """Leading dimension of a row-major [rows, cols] tensor (rows <= 1: cols)."""
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
 
 
 def _stream(stream=None) -> int:
@@ -162,15 +171,15 @@ def build_segments_dev(ids, active, n_slots: int, seg, order: int = 0, stream=No
 def shrink(pool: PoolDesc, seg, T: int, summary: Optional[Summary], x, v, launch: int = LAUNCH_EXACT,
            stream=None) -> None:
     _check(_lib.lora_shrink(ctypes.byref(pool), seg.data_ptr(), T,
-                            None if summary is None else ctypes.byref(summary), x.data_ptr(), x.stride(0),
-                            v.data_ptr(), v.stride(0), launch, _stream(stream)), "lora_shrink")
+                            None if summary is None else ctypes.byref(summary), x.data_ptr(), _ld(x),
+                            v.data_ptr(), _ld(v), launch, _stream(stream)), "lora_shrink")
 
 
 def expand(pool: PoolDesc, seg, T: int, summary: Optional[Summary], v, y, launch: int = LAUNCH_EXACT,
            stream=None) -> None:
     _check(_lib.lora_expand(ctypes.byref(pool), seg.data_ptr(), T,
-                            None if summary is None else ctypes.byref(summary), v.data_ptr(), v.stride(0),
-                            y.data_ptr(), _dtype_code(y), y.stride(0), launch, _stream(stream)), "lora_expand")
+                            None if summary is None else ctypes.byref(summary), v.data_ptr(), _ld(v),
+                            y.data_ptr(), _dtype_code(y), _ld(y), launch, _stream(stream)), "lora_expand")
 
 
 def fused_workspace_bytes(T: int, d_in: int, flags: int) -> int:
@@ -183,14 +192,14 @@ def fused_linear(base: BaseDesc, pool: Optional[PoolDesc], seg, x, v, y, flags: 
     d_out = int(y.shape[1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lora_fused_linear(ctypes.byref(base), None if pool is None else ctypes.byref(pool), _ptr(seg), T,
-                                  x.data_ptr(), x.stride(0), _ptr(v), 0 if v is None else v.stride(0),
-                                  y.data_ptr(), y.stride(0), d_in, d_out, flags, _ptr(workspace), ws_bytes,
+                                  x.data_ptr(), _ld(x), _ptr(v), 0 if v is None else _ld(v),
+                                  y.data_ptr(), _ld(y), d_in, d_out, flags, _ptr(workspace), ws_bytes,
                                   _stream(stream)), "lora_fused_linear")
 
 
 def quantize_e4m3(x, q, s_x, stream=None) -> None:
     T, d = int(x.shape[0]), int(x.shape[1])
-    _check(_lib.lora_quantize_e4m3(x.data_ptr(), T, d, x.stride(0), q.data_ptr(), q.stride(0), s_x.data_ptr(),
+    _check(_lib.lora_quantize_e4m3(x.data_ptr(), T, d, _ld(x), q.data_ptr(), _ld(q), s_x.data_ptr(),
                                    _stream(stream)), "lora_quantize_e4m3")
 
 

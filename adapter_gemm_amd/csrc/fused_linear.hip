@@ -141,8 +141,10 @@ __global__ __launch_bounds__(kThreads) void fused_gemm_kernel(FusedArgs a) {
   u32x4_t ra[AR];
   u32x4_t rw[WR];
   const u32x4_t zero4 = {0, 0, 0, 0};
-  const size_t kstep_bytes_x = MODE == kW8A8 ? 128 : 128;   // bytes of one row per k-step
-  const size_t kstep_bytes_w = MODE == kBF16 ? 128 : 64;     // fp8 widened: 64 codes = 64 bytes
+  // bytes of one row per k-step: 64 bf16, 128 fp8 codes (W8A8), or 64 fp8
+  // codes widened to bf16 while staging (W8A16)
+  const size_t kstep_bytes_x = 128;
+  const size_t kstep_bytes_w = MODE == kW8A16 ? 64 : 128;
   // element offset of this thread's chunk inside a k-step, for the d_in bound
   const int a_kofs = (tid & 7) * (MODE == kW8A8 ? 16 : 8);
   const int w_kofs = MODE == kW8A16 ? (tid & 3) * 16 : (tid & 7) * (MODE == kW8A8 ? 16 : 8);

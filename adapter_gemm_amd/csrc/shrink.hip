@@ -35,10 +35,12 @@ __device__ __forceinline__ float dot16(const u32x4_t& a, const u32x4_t& b, float
 
 template <>
 __device__ __forceinline__ float dot16<uint16_t>(const u32x4_t& a, const u32x4_t& b, float acc) {
+  // exact widening of both bf16 halves, fp32 FMA
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[q]), __builtin_bit_cast(bf16x2_t, b[q]),
-                                          acc, false);
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(bf16lo(a[q]), bf16lo(b[q]), acc);
+    acc = fmaf(bf16hi(a[q]), bf16hi(b[q]), acc);
+  }
   return acc;
 }
 

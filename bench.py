@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the multi-adapter linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--w8a8]
+
+One step is one pass of the whole hot path over one batch: device-side
+segment build -> shrink -> fused linear (base GEMM with the adapter
+up-projection in its epilogue), for every projection of the workload.
+Inputs are resident in HBM before timing; several copies of every buffer
+are rotated so that a step never finds its operands in the 256 MB
+Infinity Cache.  Prints one JSON line.
+
+The default workload is the decode batch (Llama-3-8B q_proj 4096->4096,
+bf16, 256 tokens, 64 slots of rank 16); --config selects another.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
+CACHE_BYTES = 256 << 20
+METRIC = "multi-LoRA linear tokens/s; achieved HBM GB/s (decode) & MFMA % (prefill)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_bgmv")
+    ap.add_argument("--w8a8", action="store_true", help="fp8 base: quantise activations per token")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU path is a design note, not an implementation.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import adapter_gemm_amd as agm
+    from lora_inputs import make_workload
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = make_workload(args.config)
+    T = w.T
+    print(f"# workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- one instance on the device ------------------------------------
+    touched = w.touched_slots()
+    projs = []
+    inst_bytes = 0
+    for p in w.projections:
+        A, B = p.pool(touched)            # untouched slots stay zero: never read
+        pr = {"p": p}
+        pr["A"], pr["B"] = bf16(A) if p.data_dtype == "bf16" else torch.from_numpy(A).to(dev), \
+            bf16(B) if p.data_dtype == "bf16" else torch.from_numpy(B).to(dev)
+        del A, B
+        w0 = p.w0()
+        if p.base_dtype == "fp8":
+            pr["W"], pr["ws"] = torch.from_numpy(w0[0]).to(dev), torch.from_numpy(w0[1]).to(dev)
+        elif p.base_dtype == "bf16":
+            pr["W"], pr["ws"] = bf16(w0), None
+        else:
+            pr["W"], pr["ws"] = torch.from_numpy(w0).to(dev), None
+        del w0
+        x = w.x(p)
+        pr["x"] = bf16(x) if p.data_dtype == "bf16" else torch.from_numpy(x).to(dev)
+        pr["rank"] = torch.from_numpy(p.slot_rank).to(dev)
+        pr["scale"] = torch.from_numpy(p.slot_scale).to(dev)
+        ydt = torch.bfloat16 if p.data_dtype == "bf16" else torch.float32
+        pr["y"] = torch.empty(T, p.d_out, dtype=ydt, device=dev)
+        pr["v"] = torch.empty(T, p.r_cap, dtype=torch.float32, device=dev)
+        for k in ("A", "B", "W", "x", "y", "v"):
+            inst_bytes += pr[k].numel() * pr[k].element_size()
+        projs.append(pr)
+    ids = torch.from_numpy(w.ids).to(dev)
+    act = torch.from_numpy(w.active).to(dev)
+    n_slots = w.projections[0].n_slots
+
+    # ---- rotated copies ------------------------------------------------
+    n_rot = max(1, -(-2 * CACHE_BYTES // max(inst_bytes, 1)))
+    n_rot = min(n_rot, 64)
+    flags = agm.FLAG_ACT_QUANT_E4M3 if args.w8a8 else 0
+    insts = []
+    for r in range(n_rot):
+        inst = []
+        for pr in projs:
+            c = {k: (pr[k] if r == 0 else pr[k].clone()) if isinstance(pr[k], torch.Tensor) else pr[k]
+                 for k in pr}
+            c["pool"] = agm.pool_desc(c["A"], c["B"], c["rank"], c["scale"])
+            c["base"] = agm.base_desc(c["W"], c["ws"])
+            p = c["p"]
+            c["wsp"] = None
+            if flags:
+                c["wsp"] = torch.empty(agm.fused_workspace_bytes(T, p.d_in, flags), dtype=torch.uint8, device=dev)
+            inst.append(c)
+        seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=dev)
+        insts.append((inst, seg, ids.clone(), act.clone()))
+    torch.cuda.synchronize()
+    print(f"# {n_rot} rotated instance(s) of {inst_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    n_proj = len(projs)
+
+    def step(i, ev=None):
+        inst, seg, ids_d, act_d = insts[i % n_rot]
+        if ev is not None:
+            ev["seg"][0].record(stream)
+        agm.build_segments_dev(ids_d, act_d, n_slots, seg)
+        if ev is not None:
+            ev["seg"][1].record(stream)
+        for j, c in enumerate(inst):
+            if ev is not None:
+                ev["shrink"][2 * j].record(stream)
+            agm.shrink(c["pool"], seg, T, None, c["x"], c["v"], launch=agm.LAUNCH_PERSISTENT)
+            if ev is not None:
+                ev["shrink"][2 * j + 1].record(stream)
+                ev["fused"][2 * j].record(stream)
+            agm.fused_linear(c["base"], c["pool"], seg, c["x"], c["v"], c["y"], flags=flags, workspace=c["wsp"])
+            if ev is not None:
+                ev["fused"][2 * j + 1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # (1) whole-step throughput: K back-to-back steps between two events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # (2) per-kernel durations: the same steps with events around each launch
+    def mk(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    per = {"seg": 0.0, "shrink": 0.0, "fused": 0.0}
+    for i in range(args.steps):
+        ev = {"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_proj)}
+        step(i, ev)
+        torch.cuda.synchronize()
+        per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
+        for j in range(n_proj):
+            per["shrink"] += ev["shrink"][2 * j].elapsed_time(ev["shrink"][2 * j + 1])
+            per["fused"] += ev["fused"][2 * j].elapsed_time(ev["fused"][2 * j + 1])
+    per = {k: v / args.steps for k, v in per.items()}   # ms per step
+
+    if args.calibrate_copy_mb:
+        src = torch.empty(args.calibrate_copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- algorithmic work --------------------------------------------------
+    live = w.live()
+    n_act = int(live.sum())
+    alg = {"fused_bytes": 0, "fused_flops": 0, "shrink_bytes": 0, "shrink_flops": 0}
+    for pr in projs:
+        p = pr["p"]
+        el = 2 if p.data_dtype == "bf16" else 4
+        wel = 1 if p.base_dtype == "fp8" else (2 if p.base_dtype == "bf16" else 4)
+        used = sorted(set(int(a) for a in w.ids[live]))
+        ranks = np.array([int(p.slot_rank[a]) for a in used])
+        rows_r = np.array([int(p.slot_rank[a]) for a in w.ids[live]])
+        adapters_A = int((ranks * p.d_in).sum()) * el
+        adapters_B = int((ranks * p.d_out).sum()) * el
+        v_bytes = int(rows_r.sum()) * 4
+        alg["fused_bytes"] += (p.d_out * p.d_in * wel + (4 * p.d_out if p.base_dtype == "fp8" else 0)
+                               + T * p.d_in * el + T * p.d_out * el + adapters_B + v_bytes)
+        alg["fused_flops"] += 2 * T * p.d_in * p.d_out + 2 * int(rows_r.sum()) * p.d_out
+        alg["shrink_bytes"] += adapters_A + n_act * p.d_in * el + v_bytes
+        alg["shrink_flops"] += 2 * int(rows_r.sum()) * p.d_in
+    fused_s = per["fused"] * 1e-3
+    shrink_s = per["shrink"] * 1e-3
+    fused_gbs = alg["fused_bytes"] / fused_s / 1e9
+    fused_tfs = alg["fused_flops"] / fused_s / 1e12
+    shrink_gbs = alg["shrink_bytes"] / shrink_s / 1e9
+    base = w.projections[0].base_dtype
+    mfma_dtype = "fp8" if (base == "fp8" and args.w8a8) else ("fp32" if base == "fp32" else "bf16")
+    ridge = MFMA_PEAK_TFLOPS[mfma_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ai = alg["fused_flops"] / alg["fused_bytes"]
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(fused_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        pk = MFMA_PEAK_TFLOPS[mfma_dtype]
+        roof = {"bound": "mfma", "achieved": round(fused_tfs, 1), "peak": pk, "unit": "TFLOP/s",
+                "frac": round(fused_tfs / pk, 4)}
+    roof["kernel"] = "fused_gemm_kernel"
+    roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_proj
+    roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_proj
+    roof["traffic"] = None
+
+    value = T / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if mfma_dtype == "fp8" else ("f32" if base == "fp32" else "bf16"),
+        "data": "synthetic (seeded generators; Llama-shaped; random-init adapters)",
+        "config": {"workload": f"{w.name}: {w.description}",
+                   "path": "build_segments_dev -> shrink (persistent) -> fused_linear"
+                           + (" W8A8" if args.w8a8 else (" W8A16" if base == "fp8" else "")),
+                   "T": T, "projections": n_proj, "live_rows": n_act,
+                   "distinct_adapters": len(w.touched_slots()), "rotated_instances": n_rot},
+        "roofline": roof,
+        "kernels_us_per_step": {"build_segments": round(per["seg"] * 1e3, 2),
+                                "shrink": round(per["shrink"] * 1e3, 2),
+                                "fused_linear": round(per["fused"] * 1e3, 2)},
+        "shrink_hbm": {"achieved": round(shrink_gbs, 1), "unit": "GB/s",
+                       "frac": round(shrink_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg["shrink_bytes"]},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 oracle (as it stands) on this host's cores, on a bounded
+    sample of the same workload: whole batches for as long as `seconds`
+    allows (at least one), or a slice of the rows for large workloads."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+    except ImportError:                       # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(cores) if threadpool_limits else None
+    rows = w.T
+    # large workloads: a row slice keeps the sample to ~10-30 s of CPU work
+    macs = sum(p.d_in * p.d_out for p in w.projections)
+    if macs * w.T > 4e10:
+        rows = max(16, int(4e10 // macs))
+    sel = np.arange(rows)
+    ids, act = w.ids[sel], w.active[sel]
+    touched = sorted(set(int(i) for i in ids[(ids >= 0) & (act != 0)]))
+    data = []
+    for p in w.projections:
+        A, B = p.pool(touched)
+        data.append((w.x(p)[sel], p.w0(), A, B, p.slot_rank, p.slot_scale))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.build_segments(ids, act)
+        for x, w0, A, B, rk, sc in data:
+            oracle.linear(x, w0, ids, act, A, B, rk, sc)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = cores
+    if ctx is not None:
+        try:
+            threads = max(i.get("num_threads", cores) for i in threadpool_info()) or cores
+        except Exception:
+            pass
+        ctx.unregister() if hasattr(ctx, "unregister") else None
+    return {"value": round(rows * n / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} pass(es) of the fp64 oracle (segments + {len(w.projections)} projection(s)) "
+                      f"over {rows} of {w.T} rows in {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
