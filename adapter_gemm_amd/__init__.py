@@ -76,7 +76,7 @@ def _load():
         "lora_shrink": (I32, [P, P, I32, P, P, I32, P, I32, I32, P]),
         "lora_expand": (I32, [P, P, I32, P, P, I32, P, I32, I32, I32, P]),
         "lora_fused_linear": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P, SZ, P]),
-        "lora_fused_workspace_bytes": (SZ, [I32, I32, I32]),
+        "lora_fused_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "lora_quantize_e4m3": (I32, [P, I32, I32, I32, P, I32, P, P]),
         "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lora_last_error": (ctypes.c_char_p, []),
@@ -182,8 +182,17 @@ def expand(pool: PoolDesc, seg, T: int, summary: Optional[Summary], v, y, launch
                             y.data_ptr(), _dtype_code(y), _ld(y), launch, _stream(stream)), "lora_expand")
 
 
-def fused_workspace_bytes(T: int, d_in: int, flags: int) -> int:
-    return int(_lib.lora_fused_workspace_bytes(T, d_in, flags))
+def fused_workspace_bytes(T: int, d_in: int, d_out: int, base_dtype: int, flags: int = 0) -> int:
+    """Workspace bytes of a fused call of this shape (base_dtype: F32, BF16 or FP8_E4M3)."""
+    return int(_lib.lora_fused_workspace_bytes(T, d_in, d_out, base_dtype, flags))
+
+
+def fused_workspace(T: int, d_in: int, d_out: int, base_dtype: int, flags: int = 0, device="cuda"):
+    """A workspace tensor for a fused call of this shape (None when none is needed);
+    torch's allocator hands out 256-byte aligned blocks."""
+    import torch
+    n = fused_workspace_bytes(T, d_in, d_out, base_dtype, flags)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def fused_linear(base: BaseDesc, pool: Optional[PoolDesc], seg, x, v, y, flags: int = 0, workspace=None,

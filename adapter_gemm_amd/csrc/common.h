@@ -104,6 +104,29 @@ hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_
                         const void* x, int ld_x, const float* v, int ld_v, void* y, int ld_y, int d_in,
                         int d_out, int flags, void* workspace, hipStream_t st);
 
+// Schedule of the pipelined fused linear for one call shape.
+struct FusedPlan {
+  bool dma;            // the pipelined kernel applies (d_in a multiple of its k-step)
+  int bm, bn, nk;      // tile and k-steps
+  int tiles_m, tiles_n, tiles;
+  int splits;          // k splits per tile (1 = none)
+  int lora_split;      // 1: one extra workgroup per tile runs the adapter phase
+  size_t part_bytes;   // fp32 partial tiles when splits + lora_split > 1
+  size_t counter_bytes;
+};
+
+// r_cap: the adapter pool's rank capacity, 0 without a pool
+FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap);
+bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, int base_dtype, int flags,
+                    const lora_pool_t* pool);
+hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,
+                            const int32_t* seg, int T, const void* x, int ld_x, const float* s_x, const float* v,
+                            int ld_v, void* y, int ld_y, int d_in, int d_out, int flags, void* part_ws,
+                            hipStream_t st);
+// bytes of the workspace for one fused call: [W8A8 codes + scales][partials][counters]
+size_t fused_quant_bytes(int T, int d_in, int flags, int base_dtype);
+size_t fused_workspace_bytes(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap);
+
 hipError_t launch_quantize_e4m3(const void* x, int T, int d, int ld_x, uint8_t* q, int ld_q, float* s_x,
                                 hipStream_t st);
 

@@ -1,0 +1,697 @@
+// Fused linear, pipelined form for gfx950:
+//   y[i, n] = epi( sum_k x[i, k] W0[n, k] ) + [live_i] s_a sum_j v[p(i), j] B_a[n, j]
+// ("EpiLoRA" 3.1 and Fig. 10, kernel K2: a GEMM over adapter-sorted rows
+// whose epilogue adds, per adapter group in the output tile, h_l B_l^T over
+// the tile's slice of B_l, then writes rows back in token order).
+//
+// Main loop.  A workgroup (4 waves, 2 x 2) owns a BM x BN output tile.  Every
+// k-step stages a BM x 128-byte slab of x rows (gathered through the grouped
+// order) and a BN x 128-byte (bf16, W8A8) or BN x 64-byte (fp8 codes, W8A16)
+// slab of W0 rows in one slot of an LDS ring of STAGES slots.  The slabs are
+// moved by buffer_load_dwordx4 ... lds (each lane chooses its own 16-byte
+// source, so the XOR swizzle of the LDS layout is applied on the source
+// side), with STAGES - 1 k-steps in flight; waits use explicit vmcnt counts
+// and a plain s_barrier, so no fence or compiler-inserted wait drains the
+// ring.  Rows past T and
+// channels past d_out use a buffer offset beyond the descriptor's range,
+// which the hardware turns into zeros.  MFMA: v_mfma_f32_16x16x32_bf16
+// (bf16, and W8A16 with codes widened to bf16 as fragments leave LDS) or
+// v_mfma_scale_f32_16x16x128_f8f6f4 (W8A8).
+//
+// Adapter phase.  The tile's adapter groups (segments that meet its rows)
+// become extra pipelined steps: step (group g, rank chunk c) stages
+// B_g[n0 : n0 + BN, 64c : 64c + 64] through the same ring, rank entries at or
+// beyond the adapter's rank read as zeros, and multiplies it by s_g v of the
+// group's rows, held as a bf16 tile in LDS with rows of other groups masked
+// to zero.  The products land on the same accumulators as the base GEMM.
+//
+// Split K.  When the output has too few tiles to fill the chip (decode
+// batches), the k range is split over `splits` workgroups per tile and one
+// more workgroup per tile runs the adapter phase alone.  Each writes its
+// scaled partial tile to the workspace; the last to arrive (an integer
+// counter per tile) adds the partials in split order, so the result does not
+// depend on which workgroup finished last, writes y and re-arms the counter.
+#include "common.h"
+
+#include <algorithm>
+
+namespace lora {
+namespace {
+
+constexpr int kThreads = 256;
+enum DmaMode { kBF16 = 0, kW8A16 = 1, kW8A8 = 2 };
+constexpr uint32_t kOOB = 0x80000000u;   // offset past every descriptor's range: loads return zeros
+constexpr int kLoraNBMax = 4;            // adapter-phase ring slots (at most)
+constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer, gfx9-family descriptor word 3
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+struct DmaArgs {
+  const void* x;
+  const void* W;
+  const float* w_scale;
+  const float* s_x;
+  const void* B;
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  const int32_t* seg;
+  const float* v;
+  void* y;
+  float* part;
+  int32_t* counters;
+  uint32_t x_bytes, w_bytes, v_bytes, b_bytes;   // descriptor ranges (b: the whole B pool)
+  int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out;
+  int tiles_m, tiles_n, group_m, nk, splits, lora_split;
+};
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (base, stride 0, range in bytes).
+__device__ __forceinline__ i32x4_t rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4_t r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = (int32_t)bytes;
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// 16 bytes per lane from rs + voff + soff into lds + 16 * lane.  Issued as
+// inline assembly: the compiler, which sees an LDS write it cannot bound,
+// would otherwise drain every load in flight (vmcnt(0)) before each LDS
+// read of the ring; the waits are placed by hand instead (vm_barrier).
+// Waits the compiler inserts for its own loads stay correct: vector memory
+// operations complete in issue order, so extra younger operations only make
+// a count-based wait stricter.
+__device__ __forceinline__ void dma16(const i32x4_t& rs, void* lds, uint32_t voff, uint32_t soff) {
+  // the destination is wave-uniform; make that visible to the compiler
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(m), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding and all its LDS operations are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wait for the ring slot of the current step: `ahead` (0 .. MAXA) later
+// steps of L operations each may stay in flight.
+template <int L, int MAXA>
+__device__ __forceinline__ void wait_step(int ahead) {
+  static_assert(MAXA * L <= 63, "vmcnt counts at most 63 operations");
+  if constexpr (MAXA >= 1) {
+    if (ahead >= MAXA) { vm_barrier<MAXA * L>(); return; }
+    wait_step<L, MAXA - 1>(ahead);
+  } else {
+    vm_barrier<0>();
+  }
+}
+
+// Drain this wave's vector memory operations with a wait the compiler sees:
+// afterwards it knows that none of its own loads is pending, so it places no
+// conservative vmcnt(0) of its own inside the pipelined loops that follow
+// (such a wait would also drain the hand-issued DMAs it does not see).
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Meet the other waves once this wave's LDS operations are done; vector
+// memory operations may stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_sum(int v, int* sums, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sums[wave] = incl;
+  lds_barrier();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sums[w];
+  *total = sums[0] + sums[1] + sums[2] + sums[3];
+  lds_barrier();
+  return before + incl - v;
+}
+
+__device__ __forceinline__ int sw128(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+__device__ __forceinline__ int sw64(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+// 8 e4m3 codes -> 8 bf16, exact (e4m3 values have 4 significant bits)
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 c) {
+  u32x4_t o;
+  const uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);
+    o[2 * q] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+    o[2 * q + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+  }
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+template <int BM, int BN, int MODE, int STAGES>
+__global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int WROW = MODE == kW8A16 ? 64 : 128;      // W bytes per row per k-step
+  constexpr int XS = BM * 128, WSB = BN * WROW, STAGE = XS + WSB;
+  constexpr int LX = XS / 4096, LW = WSB / 4096, L = LX + LW;   // DMA ops per wave per step
+  constexpr int RING = STAGES * STAGE;
+  constexpr int BSLICE = BN * 128;                     // one adapter step: BN channels x 64 packed ranks
+  constexpr int LB = BSLICE / 4096;
+  constexpr int XE = MODE == kW8A8 ? 1 : 2;            // x element bytes
+  constexpr int WE = MODE == kBF16 ? 2 : 1;            // W element bytes
+  static_assert(XS % 4096 == 0 && WSB % 4096 == 0, "slabs must be whole 1 KB DMA rows per wave");
+  static_assert(STAGES >= 2, "the ring needs two slots");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
+  __shared__ int g_ad[BM], g_rank[BM], g_row0[BM], g_row1[BM], t_rowseg[BM];
+  __shared__ float g_scale[BM];
+  __shared__ int s_flag, s_sums[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 15, fk = lane >> 4;
+
+  // ---- work item: (tile, split) ------------------------------------------
+  const int S_total = a.splits + a.lora_split;
+  int pid = blockIdx.x;
+  {
+    const int nblk = gridDim.x, full = (nblk / 8) * 8;   // consecutive items share an XCD
+    if (pid < full) pid = (pid & 7) * (full / 8) + (pid >> 3);
+  }
+  const int tile = pid / S_total, split = pid - tile * S_total;
+  int tm, tn;
+  {
+    const int per_group = a.group_m * a.tiles_n;
+    const int g = tile / per_group, first_m = g * a.group_m;
+    const int gm = min(a.tiles_m - first_m, a.group_m);
+    const int in = tile - g * per_group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  SegPtrs P;
+  bool has_seg = a.seg != nullptr;
+  if (has_seg) {
+    P = seg_ptrs(const_cast<int32_t*>(a.seg), a.T);
+    has_seg = seg_valid(P, a.T);
+  }
+
+  // ---- base k range of this split ----------------------------------------
+  int kbeg = 0, kend = 0;
+  if (split < a.splits) {
+    kbeg = (int)((long)split * a.nk / a.splits);
+    kend = (int)((long)(split + 1) * a.nk / a.splits);
+  }
+  const int nsteps = kend - kbeg;
+
+  // the adapter phase's row -> segment ids, fetched now and used after the
+  // main loop
+  const bool do_lora = has_seg && a.B != nullptr && (a.lora_split ? split == a.splits : true);
+  int n_active = 0, my_rowseg = -1;
+  if (do_lora) {
+    n_active = P.sum[kNActive];
+    if (tid < BM && m0 + tid < n_active) my_rowseg = P.pos_seg[m0 + tid];
+  }
+
+  // per-lane DMA source offsets (k-step offsets go into soffset)
+  uint32_t xoff[LX], woff[LW];
+#pragma unroll
+  for (int q = 0; q < LX; ++q) {
+    const int s = (wave * LX + q) * 64 + lane;
+    const int row = s >> 3, c = (s & 7) ^ (row & 7);
+    const int pos = m0 + row;
+    uint32_t o = kOOB;
+    if (pos < a.T) o = (uint32_t)((has_seg ? P.perm[pos] : pos) * a.ld_x * XE + c * 16);
+    xoff[q] = o;
+  }
+#pragma unroll
+  for (int q = 0; q < LW; ++q) {
+    const int s = (wave * LW + q) * 64 + lane;
+    int row, c;
+    if constexpr (WROW == 128) { row = s >> 3; c = (s & 7) ^ (row & 7); }
+    else { row = s >> 2; c = (s & 3) ^ ((row >> 2) & 3); }
+    const int n = n0 + row;
+    woff[q] = n < a.d_out ? (uint32_t)(n * a.ld_w * WE + c * 16) : kOOB;
+  }
+  const i32x4_t xrs = rsrc(a.x, a.x_bytes);
+  const i32x4_t wrs = rsrc(a.W, a.w_bytes);
+
+  auto issue = [&](int kt, int slot) {
+    uint8_t* st = ring + slot * STAGE;
+#pragma unroll
+    for (int q = 0; q < LX; ++q) dma16(xrs, st + (wave * LX + q) * 1024, xoff[q], (uint32_t)kt * 128u);
+#pragma unroll
+    for (int q = 0; q < LW; ++q) dma16(wrs, st + XS + (wave * LW + q) * 1024, woff[q], (uint32_t)kt * WROW);
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot) {
+    const uint8_t* As = ring + slot * STAGE;
+    const uint8_t* Ws = As + XS;
+    if constexpr (MODE == kW8A8) {
+      i32x8_t fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WM + i * 16 + frow;
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(As + sw128(row, 2 * fk));
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(As + sw128(row, 2 * fk + 1));
+        fa[i] = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WN + j * 16 + frow;
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(Ws + sw128(row, 2 * fk));
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(Ws + sw128(row, 2 * fk + 1));
+        fb[j] = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * WM + i * 16 + frow;
+          fa[i] = *reinterpret_cast<const bf16x8_t*>(As + sw128(row, kk * 4 + fk));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = wn * WN + j * 16 + frow;
+          if constexpr (MODE == kBF16) {
+            fb[j] = *reinterpret_cast<const bf16x8_t*>(Ws + sw128(row, kk * 4 + fk));
+          } else {
+            // 8 codes at byte kk * 32 + fk * 8 of the 64-byte row
+            const uint2 c8 = *reinterpret_cast<const uint2*>(Ws + sw64(row, kk * 2 + (fk >> 1)) + (fk & 1) * 8);
+            fb[j] = e4m3x8_to_bf16(c8);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop -----------------------------------------------------------
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nsteps) issue(kbeg + p, p);
+  for (int t = 0; t < nsteps; ++t) {
+    wait_step<L, STAGES - 2>(min(STAGES - 2, nsteps - 1 - t));
+    if (t + STAGES - 1 < nsteps) issue(kbeg + t + STAGES - 1, (t + STAGES - 1) % STAGES);
+    compute(t % STAGES);
+  }
+
+  const int row_base = m0 + wm * WM;   // first grouped position of this wave's rows
+  const int col_base = n0 + wn * WN;
+  const int ocol = lane & 15, orow = (lane >> 4) * 4;
+
+  // base scales (fp8): w_scale[n] [* s_x[row]]
+  if constexpr (MODE != kBF16) {
+    if (nsteps > 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = col_base + j * 16 + ocol;
+        const float sw = n < a.d_out ? a.w_scale[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float s = sw;
+            if constexpr (MODE == kW8A8) {
+              const int pos = row_base + i * 16 + orow + e;
+              if (pos < a.T) s *= a.s_x[has_seg ? P.perm[pos] : pos];
+            }
+            acc[i][j][e] *= s;
+          }
+        }
+      }
+    }
+  }
+
+  // ---- adapter phase -------------------------------------------------------
+  // The tile's groups are laid end to end along one packed rank axis: group
+  // g occupies chunks [off_g, off_g + ceil(r_g / 8)) of 8 ranks.  Packed
+  // A[row, k] is s_g v[row, j] when the row belongs to the group owning chunk
+  // k / 8 (j its rank index inside the group), else 0; packed B[n, k] is
+  // B_g[n, j].  A x B^T over the packed axis is exactly the sum of the
+  // groups' s_g v B_g^T, run as dense 64-wide MFMA steps.
+  if (do_lora) {
+    const int pe = min(m0 + BM, n_active);
+    if (m0 < pe) {
+      vm_barrier<0>();                          // ring free: every wave is past its last main step
+      // raw fp32 v rows [m0, pe) x r_cap -> ring[0, BM * r_cap * 4); rows at
+      // or past pe read as zeros.  Logical 16-byte chunk c4 of row r sits at
+      // chunk (c4 + r / vd) mod rq of the row, so that the 16 rows a fragment
+      // read touches fall in distinct LDS banks.
+      const int rq = a.r_cap / 4;               // 16-byte chunks per v row
+      const int vd = rq >= 16 ? 1 : 16 / rq;
+      const int vchunks = BM * rq;              // a multiple of 128
+      const i32x4_t vrs = rsrc(a.v, a.v_bytes);
+      for (int c0 = wave * 64; c0 < vchunks; c0 += 256) {
+        const int c = c0 + lane;
+        const int row = c / rq, phys = c - row * rq;
+        const int c4 = (phys + rq - (row / vd) % rq) % rq;
+        const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
+        dma16(vrs, ring + c0 * 16, o, 0u);
+      }
+      // group table (segments meeting the tile's live rows)
+      if (tid < BM) t_rowseg[tid] = my_rowseg;
+      lds_barrier();
+      const int s_first = t_rowseg[0];
+      const int ng = t_rowseg[pe - 1 - m0] - s_first + 1;
+      int gad = 0, grk = 0, gr0 = 0, gr1 = 0;
+      float gsc = 0.f;
+      if (tid < ng) {
+        gad = P.seg_adapter[s_first + tid];
+        gr0 = max(P.seg_start[s_first + tid], m0) - m0;         // the group's rows, tile-local
+        gr1 = min(P.seg_start[s_first + tid + 1], pe) - m0;
+        grk = a.slot_rank[gad];
+        gsc = a.slot_scale[gad];
+      }
+      int n_chunks;
+      const int w8 = (grk + 7) / 8;
+      const int off = block_exclusive_sum(w8, s_sums, &n_chunks);
+      const int cm_off = BM * a.r_cap * 4;
+      uint16_t* cm = reinterpret_cast<uint16_t*>(ring + cm_off);
+      const int bsl_off = (cm_off + BM * a.r_cap / 4 + 1023) & ~1023;
+      uint8_t* bsl = ring + bsl_off;
+      const int nb = min(kLoraNBMax, (RING - bsl_off) / BSLICE);   // >= 2 by the host plan
+      if (tid < ng) {
+        g_ad[tid] = gad;
+        g_row0[tid] = gr0;
+        g_row1[tid] = gr1;
+        g_rank[tid] = grk;
+        g_scale[tid] = gsc;
+        for (int j = 0; j < w8; ++j) cm[off + j] = (uint16_t)((tid << 4) | j);
+      }
+      vm_drain();
+      lds_barrier();
+      const int nls = (n_chunks + 7) / 8;
+      const i32x4_t brs = rsrc(a.B, a.b_bytes);
+
+      auto issue_b = [&](int t) {
+        uint8_t* dst = bsl + (t % nb) * BSLICE;
+#pragma unroll
+        for (int q = 0; q < LB; ++q) {
+          const int s = (wave * LB + q) * 64 + lane;
+          const int n = s >> 3, c = (s & 7) ^ (n & 7);
+          const int kc = t * 8 + c;
+          uint32_t o = kOOB;
+          if (kc < n_chunks && n0 + n < a.d_out) {
+            const int e = cm[kc], g = e >> 4, j8 = e & 15;
+            o = (uint32_t)((((size_t)g_ad[g] * a.d_out + n0 + n) * a.r_cap + j8 * 8) * 2);
+          }
+          dma16(brs, dst + (wave * LB + q) * 1024, o, 0u);
+        }
+      };
+
+      const float* V = reinterpret_cast<const float*>(ring);
+      for (int t = 0; t < nb - 1 && t < nls; ++t) issue_b(t);
+      for (int t = 0; t < nls; ++t) {
+        wait_step<LB, kLoraNBMax - 2>(min(nb - 2, nls - 1 - t));
+        if (t + nb - 1 < nls) issue_b(t + nb - 1);
+        const uint8_t* Bs = bsl + (t % nb) * BSLICE;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          // the groups of this half step are consecutive, so their rows are
+          // one range [r_lo, r_hi); fragments outside it multiply zeros
+          const int kc_lo = t * 8 + kk * 4;
+          if (kc_lo >= n_chunks) break;
+          const int kc_hi = min(kc_lo + 3, n_chunks - 1);
+          const int r_lo = g_row0[cm[kc_lo] >> 4], r_hi = g_row1[cm[kc_hi] >> 4];
+          const int kc = kc_lo + fk;            // this lane's packed chunk
+          int g = -1, j8 = 0, rk = 0;
+          float sc = 0.f;
+          if (kc < n_chunks) {
+            const int e = cm[kc];
+            g = e >> 4;
+            j8 = e & 15;
+            rk = g_rank[g];
+            sc = g_scale[g];
+          }
+          const int lim = rk - j8 * 8;          // ranks of this chunk below the group's rank
+          bf16x8_t fb[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int row = wn * WN + j * 16 + frow;
+            u32x4_t u = *reinterpret_cast<const u32x4_t*>(Bs + sw128(row, kk * 4 + fk));
+            if (lim < 8) {                      // rank padding inside the chunk, or no chunk
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (2 * e >= lim) u[e] = 0;
+                else if (2 * e + 1 >= lim) u[e] &= 0xffffu;
+              }
+            }
+            fb[j] = __builtin_bit_cast(bf16x8_t, u);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int f0 = wm * WM + i * 16;
+            if (f0 + 16 <= r_lo || f0 >= r_hi) continue;
+            const int r = f0 + frow;
+            u32x4_t ua = {0, 0, 0, 0};
+            if (g >= 0 && t_rowseg[r] - s_first == g) {
+              const float* vr = V + r * a.r_cap;
+              const int sh = r / vd;
+              const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vr + ((2 * j8 + sh) % rq) * 4);
+              const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vr + ((2 * j8 + 1 + sh) % rq) * 4);
+              float w[8];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                w[e] = e < lim ? sc * v0[e] : 0.f;
+                w[4 + e] = 4 + e < lim ? sc * v1[e] : 0.f;
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ua[e] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
+            }
+            const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, ua);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- output ----------------------------------------------------------------
+  uint16_t* __restrict__ Y = static_cast<uint16_t*>(a.y);
+  if (S_total > 1) {
+    // Hand-off without L2-wide fences: partial tiles are written and read
+    // with agent-scope atomic accesses (coherent across XCDs at the memory
+    // side, never left dirty in or read stale from an XCD's L2); every wave
+    // drains its stores (vmcnt(0)) before the barrier that precedes the
+    // counter increment, and the reads are issued only after the increment
+    // that found all other partials counted.
+    float* mine = a.part + ((size_t)tile * S_total + split) * (BM * BN) + (size_t)wave * TM * TN * 256;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(mine + ((i * TN + j) * 64 + lane) * 4 + e, acc[i][j][e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    vm_barrier<0>();
+    if (tid == 0)
+      s_flag = __hip_atomic_fetch_add(&a.counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S_total - 1;
+    vm_barrier<0>();
+    if (!s_flag) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S_total; ++s) {
+      const float* src = a.part + ((size_t)tile * S_total + s) * (BM * BN) + (size_t)wave * TM * TN * 256;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][e] += __hip_atomic_load(src + ((i * TN + j) * 64 + lane) * 4 + e, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = row_base + i * 16 + orow + e;
+      if (pos >= a.T) continue;
+      const int row = has_seg ? P.perm[pos] : pos;
+      uint16_t* yr = Y + (size_t)row * a.ld_y;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = col_base + j * 16 + ocol;
+        if (n < a.d_out) yr[n] = f32_to_bf16(acc[i][j][e]);
+      }
+    }
+  }
+}
+
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+template <int BM, int BN, int MODE, int STAGES>
+hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
+  const int S_total = a.splits + a.lora_split;
+  if (S_total > 1) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, a.counters, pl.tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((fused_dma_kernel<BM, BN, MODE, STAGES>), dim3(pl.tiles * S_total), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
+  if constexpr (MODE != kW8A16) {
+    if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3>(a, pl, st);
+  }
+  if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4>(a, pl, st);
+  return launch_cfg<64, 64, MODE, 4>(a, pl, st);
+}
+
+}  // namespace
+
+namespace {
+// LDS ring of one configuration, and whether the adapter phase (fp32 v rows,
+// the packed chunk map and at least two B slices) fits in it.
+int ring_bytes(int bm, int bn, bool w8a16, int stages) { return stages * (bm * 128 + bn * (w8a16 ? 64 : 128)); }
+bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap) {
+  if (r_cap <= 0) return true;
+  const int used = (bm * r_cap * 4 + bm * r_cap / 4 + 1023) & ~1023;
+  return ring_bytes(bm, bn, w8a16, stages) - used >= 2 * bn * 128;
+}
+}  // namespace
+
+FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap) {
+  FusedPlan pl{};
+  pl.dma = false;
+  if (T <= 0 || d_out <= 0 || d_in <= 0) return pl;
+  if (base_dtype != LORA_BF16 && base_dtype != LORA_FP8_E4M3) return pl;
+  const bool w8a8 = base_dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
+  const bool w8a16 = base_dtype == LORA_FP8_E4M3 && !w8a8;
+  const int kb = w8a8 ? 128 : 64;
+  if (d_in % kb) return pl;
+  // the largest tile that still gives every CU a tile (>= 256 tiles), else
+  // 64 x 64; 256-row tiles are not built for the widened-fp8 mode
+  struct Cfg { int bm, bn, stages; };
+  const Cfg cands[] = {{256, 128, 3}, {128, 128, 4}, {64, 64, 4}};
+  const Cfg* pick = nullptr;
+  for (const Cfg& c : cands) {
+    if (c.bm == 256 && w8a16) continue;
+    if (!lora_fits(c.bm, c.bn, w8a16, c.stages, r_cap)) continue;
+    const long tiles = (long)((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
+    if (tiles >= 256 || c.bm == 64) { pick = &c; break; }
+  }
+  if (!pick) return pl;
+  pl.dma = true;
+  pl.bm = pick->bm;
+  pl.bn = pick->bn;
+  pl.nk = d_in / kb;
+  pl.tiles_m = (T + pl.bm - 1) / pl.bm;
+  pl.tiles_n = (d_out + pl.bn - 1) / pl.bn;
+  pl.tiles = pl.tiles_m * pl.tiles_n;
+  // very small outputs: split k over up to 4 workgroups per tile (at least 8
+  // k-steps each), plus one for the adapter phase
+  pl.splits = 1;
+  if (pl.tiles < 64) pl.splits = std::max(1, std::min(4, pl.nk / 8));
+  pl.lora_split = (pl.splits > 1 && r_cap > 0) ? 1 : 0;
+  const int S_total = pl.splits + pl.lora_split;
+  pl.part_bytes = S_total > 1 ? (size_t)pl.tiles * S_total * pl.bm * pl.bn * sizeof(float) : 0;
+  pl.counter_bytes = S_total > 1 ? (size_t)pl.tiles * sizeof(int32_t) : 0;
+  return pl;
+}
+
+size_t fused_quant_bytes(int T, int d_in, int flags, int base_dtype) {
+  if (!(flags & LORA_FLAG_ACT_QUANT_E4M3) || base_dtype != LORA_FP8_E4M3 || T <= 0 || d_in <= 0) return 0;
+  const size_t ld_q = (size_t)(d_in + 15) / 16 * 16;
+  return ((size_t)T * ld_q + (size_t)T * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t fused_workspace_bytes(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap) {
+  const FusedPlan pl = plan_fused(T, d_in, d_out, base_dtype, flags, r_cap);
+  return fused_quant_bytes(T, d_in, flags, base_dtype) + (pl.dma ? pl.part_bytes + pl.counter_bytes : 0);
+}
+
+bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, int base_dtype, int flags,
+                    const lora_pool_t* pool) {
+  if (!pl.dma) return false;
+  const bool w8a8 = base_dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
+  const long lim = 0x7fffffffL;
+  const long xb = (long)T * ld_x * (w8a8 ? 1 : 2);
+  const long wb = (long)d_out * ld_w * (base_dtype == LORA_BF16 ? 2 : 1);
+  if (xb > lim || wb > lim) return false;
+  if (pool && (long)pool->n_slots * pool->d_out * pool->r_cap * 2 > lim) return false;
+  return true;
+}
+
+hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,
+                            const int32_t* seg, int T, const void* x, int ld_x, const float* s_x, const float* v,
+                            int ld_v, void* y, int ld_y, int d_in, int d_out, int flags, void* part_ws,
+                            hipStream_t st) {
+  DmaArgs a;
+  const bool w8a8 = base.dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
+  a.x = x;
+  a.W = base.W;
+  a.w_scale = base.w_scale;
+  a.s_x = s_x;
+  a.B = pool ? pool->B : nullptr;
+  a.slot_rank = pool ? pool->slot_rank : nullptr;
+  a.slot_scale = pool ? pool->slot_scale : nullptr;
+  a.seg = seg;
+  a.v = v;
+  a.y = y;
+  a.part = static_cast<float*>(part_ws);
+  a.counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(part_ws) + pl.part_bytes);
+  a.x_bytes = (uint32_t)((long)T * ld_x * (w8a8 ? 1 : 2));
+  a.w_bytes = (uint32_t)((long)d_out * base.ld_w * (base.dtype == LORA_BF16 ? 2 : 1));
+  a.b_bytes = pool ? (uint32_t)((long)pool->n_slots * pool->d_out * pool->r_cap * 2) : 0;
+  a.v_bytes = pool ? (uint32_t)((long)T * ld_v * 4) : 0;
+  a.r_cap = pool ? pool->r_cap : 0;
+  a.ld_v = ld_v;
+  a.ld_y = ld_y;
+  a.ld_x = ld_x;
+  a.ld_w = base.ld_w;
+  a.T = T;
+  a.d_in = d_in;
+  a.d_out = d_out;
+  a.tiles_m = pl.tiles_m;
+  a.tiles_n = pl.tiles_n;
+  a.group_m = std::min(pl.tiles_m, 8);
+  a.nk = pl.nk;
+  a.splits = pl.splits;
+  a.lora_split = pool ? pl.lora_split : 0;
+  if (base.dtype == LORA_BF16) return launch_mode<kBF16>(a, pl, st);
+  if (w8a8) return launch_mode<kW8A8>(a, pl, st);
+  return launch_mode<kW8A16>(a, pl, st);
+}
+
+}  // namespace lora

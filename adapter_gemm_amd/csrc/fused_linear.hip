@@ -506,17 +506,30 @@ hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_
   a.T = T;
   a.d_in = d_in;
   a.d_out = d_out;
-  if (base.dtype == LORA_BF16) return launch_mode<kBF16>(a, st);
-  if (!(flags & LORA_FLAG_ACT_QUANT_E4M3)) return launch_mode<kW8A16>(a, st);
-  // W8A8: quantise x per token into the workspace, then the fp8 x fp8 product
-  uint8_t* q = static_cast<uint8_t*>(workspace);
-  const int ld_q = (d_in + 15) / 16 * 16;
-  float* s_x = reinterpret_cast<float*>(q + (size_t)T * ld_q);
-  hipError_t e = launch_quantize_e4m3(x, T, d_in, ld_x, q, ld_q, s_x, st);
-  if (e != hipSuccess) return e;
-  a.x = q;
-  a.ld_x = ld_q;
+  const FusedPlan pl = plan_fused(T, d_in, d_out, base.dtype, flags, pool ? pool->r_cap : 0);
+  const bool w8a8 = base.dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
+  const size_t qbytes = fused_quant_bytes(T, d_in, flags, base.dtype);
+  const void* xin = x;
+  int ld_in = ld_x;
+  float* s_x = nullptr;
+  if (w8a8) {
+    // quantise x per token into the workspace, then the fp8 x fp8 product
+    uint8_t* q = static_cast<uint8_t*>(workspace);
+    const int ld_q = (d_in + 15) / 16 * 16;
+    s_x = reinterpret_cast<float*>(q + (size_t)T * ld_q);
+    hipError_t e = launch_quantize_e4m3(x, T, d_in, ld_x, q, ld_q, s_x, st);
+    if (e != hipSuccess) return e;
+    xin = q;
+    ld_in = ld_q;
+  }
+  if (fused_dma_fits(pl, T, ld_in, d_out, base.ld_w, base.dtype, flags, pool))
+    return launch_fused_dma(pl, base, pool, seg, T, xin, ld_in, s_x, v, ld_v, y, ld_y, d_in, d_out, flags,
+                            static_cast<uint8_t*>(workspace) + qbytes, st);
+  a.x = xin;
+  a.ld_x = ld_in;
   a.s_x = s_x;
+  if (base.dtype == LORA_BF16) return launch_mode<kBF16>(a, st);
+  if (!w8a8) return launch_mode<kW8A16>(a, st);
   return launch_mode<kW8A8>(a, st);
 }
 

@@ -209,10 +209,11 @@ int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
                                         static_cast<hipStream_t>(stream)));
 }
 
-size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t flags) {
-  if (!(flags & LORA_FLAG_ACT_QUANT_E4M3) || T <= 0 || d_in <= 0) return 0;
-  const size_t ld_q = (size_t)(d_in + 15) / 16 * 16;
-  return (size_t)T * ld_q + (size_t)T * sizeof(float) + 16;
+size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags) {
+  if (T <= 0 || d_in <= 0 || d_out <= 0) return 0;
+  if (base_dtype != LORA_F32 && base_dtype != LORA_BF16 && base_dtype != LORA_FP8_E4M3) return 0;
+  // the smallest rank capacity admits every schedule: its size covers the others
+  return lora::fused_workspace_bytes(T, d_in, d_out, base_dtype, flags, 8);
 }
 
 int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
@@ -244,9 +245,10 @@ int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const in
   if (bt != LORA_FP8_E4M3 && base->ld_w % 8) return LORA_E_ALIGN;
   if (!aligned16(x) || !aligned16(y) || !aligned16(base->W)) return LORA_E_ALIGN;
   if (x == y) return LORA_E_ARG;
-  if (flags & LORA_FLAG_ACT_QUANT_E4M3) {
-    if (!workspace || workspace_bytes < lora_fused_workspace_bytes(T, d_in, flags)) return LORA_E_SIZE;
-    if (!aligned16(workspace)) return LORA_E_ALIGN;
+  const size_t need = lora::fused_workspace_bytes(T, d_in, d_out, bt, flags, pool ? pool->r_cap : 0);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return LORA_E_SIZE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LORA_E_ALIGN;
   }
   if (T == 0 || d_out == 0) return LORA_OK;
   return hip_status(lora::launch_fused(*base, pool, const_cast<int32_t*>(seg), T, x, ld_x, v, ld_v, y, ld_y, d_in,

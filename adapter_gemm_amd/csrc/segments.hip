@@ -5,88 +5,135 @@
 // gather inputs and scatter results through the adapter-grouped row-index
 // array I_a (here `perm`), with m_a = |I_a|; 3.1.4 Eqs. 7-8: the row bound R.
 //
-// One workgroup of 1024 threads does the whole build (decode/prefill batches
-// are a few thousand rows; the build is a handful of microseconds):
-//   1. histogram of live ids in LDS (and first appearance for order = 1),
+// One workgroup does the whole build (256 threads for batches of at most 256
+// rows, else 1024); rows are taken in chunks of one row per thread (a batch
+// that fits one chunk keeps its rows in registers from step 1 to step 3):
+//   1. per wave, a ballot loop splits the wave's live rows into runs of equal
+//      id: every lane learns its rank among equal ids inside the wave, and one
+//      leader lane per distinct id adds the run length to an LDS histogram
+//      (for order = 1 it also records the first row of the id);
 //   2. segment index per adapter (exclusive scan of "present", or of first
-//      appearances over the rows), segment lengths and starts,
-//   3. stable scatter: rows are visited in batch order, 1024 at a time; the
-//      16 waves of a chunk take turns, each placing its 64 rows with ballots
-//      (rows of equal id inside a wave get consecutive slots in lane order),
-//      so the grouping is deterministic and stable without a sort,
-//   4. per-segment row tiles of 16 and 64 rows, m_max, R and the summary.
+//      appearances over the rows), segment starts, row tiles of 16 and 64
+//      rows, m_max and R;
+//   3. the chunk's waves visit a per-adapter cursor in wave order: each
+//      leader takes its run's base position and advances the cursor, so rows
+//      land in batch order inside every segment (stable, deterministic) while
+//      the ballot work itself runs in all waves at once.
 #include "common.h"
 
 namespace lora {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
+struct BuildLds {
+  int wave_sums[17];
+  int err, nseg, nact, mmax, dead_run;
+  int wave_dead[16];
+  int run_base[16][64];     // per wave: base position of the run led by each lane
+};
 
-// exclusive scan of one value per thread over the workgroup; returns the
-// prefix and writes the total to *total (valid for all threads after return)
+// exclusive scan of one value per thread over the workgroup; the total is
+// written to *total for every thread
+template <int THREADS>
 __device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
+  constexpr int kWaves = THREADS / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(incl, o, 64);
+    const int t = __shfl_up(incl, o, 64);
     if (lane >= o) incl += t;
   }
   if (lane == 63) wave_sums[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    int s = lane < kWaves ? wave_sums[lane] : 0;
+    const int s = lane < kWaves ? wave_sums[lane] : 0;
     int si = s;
 #pragma unroll
     for (int o = 1; o < kWaves; o <<= 1) {
-      int t = __shfl_up(si, o, 64);
+      const int t = __shfl_up(si, o, 64);
       if (lane >= o) si += t;
     }
-    if (lane < kWaves) wave_sums[lane] = si - s;      // exclusive wave offsets
-    if (lane == kWaves - 1) wave_sums[kWaves] = si;   // total
+    if (lane < kWaves) wave_sums[lane] = si - s;
+    if (lane == kWaves - 1) wave_sums[kWaves] = si;
   }
   __syncthreads();
-  int res = wave_sums[wave] + incl - v;
+  const int res = wave_sums[wave] + incl - v;
   *total = wave_sums[kWaves];
-  __syncthreads();                                     // wave_sums reusable
+  __syncthreads();
   return res;
 }
 
-__global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t* __restrict__ ids,
-                                                                  const uint8_t* __restrict__ active, int T,
-                                                                  int N, int order, int32_t* __restrict__ seg) {
+// Runs of equal live ids inside one wave.  Returns the lane's rank among the
+// live lanes of its id (lower lanes first); `leader` = lowest lane of the id,
+// `run` = number of lanes of the id (valid in the leader lane).
+__device__ __forceinline__ int wave_runs(bool live, int id, int lane, int& leader, int& run) {
+  uint64_t remaining = __ballot(live);
+  int rank = 0;
+  leader = -1;
+  run = 0;
+  while (remaining) {
+    const int l = __ffsll((unsigned long long)remaining) - 1;
+    const int key = __shfl(id, l, 64);
+    const uint64_t m = __ballot(live && id == key);
+    if (live && id == key) {
+      rank = __popcll(m & lanemask_lt());
+      leader = l;
+    }
+    if (lane == l) run = __popcll(m);
+    remaining &= ~m;
+  }
+  return rank;
+}
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* __restrict__ ids,
+                                                                 const uint8_t* __restrict__ active, int T, int N,
+                                                                 int order, int32_t* __restrict__ seg) {
+  constexpr int kWaves = THREADS / 64;
   extern __shared__ int lds[];
   int* cnt = lds;           // [N] live rows per adapter, later the placement cursor
   int* sidx = lds + N;      // [N] segment index per adapter (order 1: first row first)
-  int* slen = lds + 2 * N;  // [N] segment lengths in segment order
-  __shared__ int wave_sums[kWaves + 1];
-  __shared__ int s_err, s_nseg, s_nact, s_mmax, s_inact, s_run;
+  int* sst = lds + 2 * N;   // [N] segment lengths, then segment starts, in segment order
+  __shared__ BuildLds sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   SegPtrs P = seg_ptrs(seg, T);
 
-  for (int a = tid; a < N; a += kThreads) {
+  for (int a = tid; a < N; a += THREADS) {
     cnt[a] = 0;
     sidx[a] = (order == 1) ? 0x7fffffff : 0;
-    slen[a] = 0;
   }
-  if (tid == 0) { s_err = 0; s_mmax = 0; s_inact = 0; s_run = 0; }
+  if (tid == 0) { sh.err = 0; sh.mmax = 0; sh.dead_run = 0; }
   __syncthreads();
 
-  // 1. histogram, validation, first appearance
-  for (int i = tid; i < T; i += kThreads) {
-    int id = ids[i];
-    if (id < -1 || id >= N) {
-      s_err = 1;
-    } else if (id >= 0 && (active == nullptr || active[i] != 0)) {
-      atomicAdd(&cnt[id], 1);
-      if (order == 1) atomicMin(&sidx[id], i);
+  // 1. histogram by runs, validation, first appearance.  A batch of at most
+  // THREADS rows is one chunk: its ids, live flags and runs stay in registers
+  // for the scatter.
+  const bool single = T <= THREADS;
+  int r_id = -1, r_rank = 0, r_leader = -1, r_run = 0;
+  bool r_live = false;
+  for (int base = 0; base < T; base += THREADS) {
+    const int i = base + tid;
+    int id = -1;
+    bool live = false;
+    if (i < T) {
+      id = ids[i];
+      if (id < -1 || id >= N) sh.err = 1;
+      else live = id >= 0 && (active == nullptr || active[i] != 0);
+    }
+    if (base + wave * 64 < T) {
+      int leader, run;
+      const int rank = wave_runs(live, id, lane, leader, run);
+      if (run > 0) {
+        atomicAdd(&cnt[id], run);
+        if (order == 1) atomicMin(&sidx[id], i);
+      }
+      if (single) { r_id = id; r_live = live; r_rank = rank; r_leader = leader; r_run = run; }
     }
   }
   __syncthreads();
-  if (s_err) {
+  if (sh.err) {
     if (tid == 0) {
       for (int w = 0; w < kSegHeader; ++w) P.sum[w] = 0;
       P.sum[kRows] = T;
@@ -98,62 +145,61 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   // 2. segment index of each present adapter
   if (order == 0) {
     int run = 0;
-    for (int base = 0; base < N; base += kThreads) {
-      int a = base + tid;
-      int present = (a < N && cnt[a] > 0) ? 1 : 0;
+    for (int base = 0; base < N; base += THREADS) {
+      const int a = base + tid;
+      const int present = (a < N && cnt[a] > 0) ? 1 : 0;
       int tot;
-      int ex = block_exclusive_scan(present, wave_sums, &tot);
+      const int ex = block_exclusive_scan<THREADS>(present, sh.wave_sums, &tot);
       if (present) sidx[a] = run + ex;
       run += tot;
     }
-    if (tid == 0) s_nseg = run;
+    if (tid == 0) sh.nseg = run;
   } else {
     // rows that are the first appearance of their adapter, in batch order;
-    // assigned indices are stored negated so that a later row never matches
+    // indices are stored negated so that a later row never matches
     int run = 0;
-    for (int base = 0; base < T; base += kThreads) {
-      int i = base + tid;
+    for (int base = 0; base < T; base += THREADS) {
+      const int i = base + tid;
       int id = -1, first = 0;
       if (i < T) {
         id = ids[i];
-        bool live = id >= 0 && (active == nullptr || active[i] != 0);
+        const bool live = id >= 0 && (active == nullptr || active[i] != 0);
         first = (live && sidx[id] == i) ? 1 : 0;
       }
       int tot;
-      int ex = block_exclusive_scan(first, wave_sums, &tot);   // contains barriers
+      const int ex = block_exclusive_scan<THREADS>(first, sh.wave_sums, &tot);
       if (first) sidx[id] = -(run + ex) - 1;
       run += tot;
-      __syncthreads();
     }
-    for (int a = tid; a < N; a += kThreads)
+    __syncthreads();
+    for (int a = tid; a < N; a += THREADS)
       if (cnt[a] > 0) sidx[a] = -sidx[a] - 1;
-    if (tid == 0) s_nseg = run;
+    if (tid == 0) sh.nseg = run;
   }
   __syncthreads();
-  const int S = s_nseg;
+  const int S = sh.nseg;
 
-  // segment lengths and adapters in segment order
-  for (int a = tid; a < N; a += kThreads) {
+  for (int a = tid; a < N; a += THREADS) {
     if (cnt[a] > 0) {
-      slen[sidx[a]] = cnt[a];
+      sst[sidx[a]] = cnt[a];
       P.seg_adapter[sidx[a]] = a;
-      atomicMax(&s_mmax, cnt[a]);
+      atomicMax(&sh.mmax, cnt[a]);
     }
   }
   __syncthreads();
 
-  // segment starts; tiles
+  // segment starts and row tiles
   {
     int run = 0, run_s = 0, run_l = 0;
-    for (int base = 0; base < S; base += kThreads) {
-      int s = base + tid;
-      int len = s < S ? slen[s] : 0;
-      int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
-      int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
+    for (int base = 0; base < S; base += THREADS) {
+      const int s = base + tid;
+      const int len = s < S ? sst[s] : 0;
+      const int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
+      const int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
       int tot, tot_s, tot_l;
-      int st = block_exclusive_scan(len, wave_sums, &tot) + run;
-      int os = block_exclusive_scan(ns, wave_sums, &tot_s) + run_s;
-      int ol = block_exclusive_scan(nl, wave_sums, &tot_l) + run_l;
+      const int st = block_exclusive_scan<THREADS>(len, sh.wave_sums, &tot) + run;
+      const int os = block_exclusive_scan<THREADS>(ns, sh.wave_sums, &tot_s) + run_s;
+      const int ol = block_exclusive_scan<THREADS>(nl, sh.wave_sums, &tot_l) + run_l;
       if (s < S) {
         P.seg_start[s] = st;
         for (int t = 0; t < ns; ++t) {
@@ -164,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
           P.tiles_large[2 * (ol + t)] = st + t * LORA_TILE_LARGE;
           P.tiles_large[2 * (ol + t) + 1] = s;
         }
-        slen[s] = st;               // slen now holds the start of segment s
+        sst[s] = st;
       }
       run += tot;
       run_s += tot_s;
@@ -172,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
     }
     if (tid == 0) {
       P.seg_start[S] = run;
-      s_nact = run;
+      sh.nact = run;
       P.sum[kNTilesSmall] = run_s;
       P.sum[kNTilesLarge] = run_l;
     }
@@ -180,54 +226,61 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   __syncthreads();
 
   // placement cursor per adapter = start of its segment
-  for (int a = tid; a < N; a += kThreads)
-    if (cnt[a] > 0) cnt[a] = slen[sidx[a]];
+  for (int a = tid; a < N; a += THREADS)
+    if (cnt[a] > 0) cnt[a] = sst[sidx[a]];
   __syncthreads();
 
-  // 3. stable scatter, chunk by chunk; waves take turns within a chunk
-  const int n_active = s_nact;
-  for (int base = 0; base < T; base += kThreads) {
+  // 3. stable scatter, chunk by chunk
+  const int n_active = sh.nact;
+  for (int base = 0; base < T; base += THREADS) {
     const int i = base + tid;
-    int id = -1;
-    bool live = false;
-    if (i < T) {
-      id = ids[i];
-      live = id >= 0 && (active == nullptr || active[i] != 0);
+    int id = r_id, leader = r_leader, run = r_run, rank = r_rank;
+    bool live = r_live;
+    if (!single) {
+      id = -1;
+      live = false;
+      if (i < T) {
+        id = ids[i];
+        live = id >= 0 && (active == nullptr || active[i] != 0);
+      }
+      leader = -1;
+      run = 0;
+      rank = 0;
+      if (base + wave * 64 < T) rank = wave_runs(live, id, lane, leader, run);
     }
-    for (int w = 0; w < kWaves; ++w) {
-      if (wave == w) {
-        const uint64_t live_mask = __ballot(live);
-        const uint64_t dead_mask = __ballot(i < T && !live);
-        uint64_t remaining = live_mask;
-        int pos = -1;
-        while (remaining) {
-          const int leader = __ffsll((unsigned long long)remaining) - 1;
-          const int key = __shfl(id, leader, 64);
-          const uint64_t m = __ballot(live && id == key);
-          int b = 0;
-          if (lane == leader) {
-            b = cnt[key];
-            cnt[key] = b + __popcll(m);
-          }
-          b = __shfl(b, leader, 64);
-          if (live && id == key) pos = b + __popcll(m & lanemask_lt());
-          remaining &= ~m;
-        }
-        const int dead_base = s_inact;
-        if (i < T && !live) pos = n_active + dead_base + __popcll(dead_mask & lanemask_lt());
-        if (i < T) {
-          P.perm[pos] = i;
-          P.pos_seg[pos] = live ? sidx[id] : -1;
-        }
-        if (lane == 0) s_inact = dead_base + __popcll(dead_mask);
+    const uint64_t dead_mask = __ballot(i < T && !live);
+    if (lane == 0) sh.wave_dead[wave] = __popcll(dead_mask);
+    // waves take their cursor positions in wave order
+    const int chunk_waves = min(kWaves, (T - base + 63) / 64);
+    for (int w = 0; w < chunk_waves; ++w) {
+      if (wave == w && run > 0) {
+        const int b = cnt[id];
+        cnt[id] = b + run;
+        sh.run_base[wave][lane] = b;
       }
       __syncthreads();
     }
+    int dead_before = sh.dead_run;
+    for (int w = 0; w < wave; ++w) dead_before += sh.wave_dead[w];
+    if (i < T) {
+      int pos;
+      if (live) pos = sh.run_base[wave][leader] + rank;
+      else pos = n_active + dead_before + __popcll(dead_mask & lanemask_lt());
+      P.perm[pos] = i;
+      P.pos_seg[pos] = live ? sidx[id] : -1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int d = 0;
+      for (int w = 0; w < kWaves; ++w) d += sh.wave_dead[w];
+      sh.dead_run += d;
+    }
+    __syncthreads();
   }
 
   // 4. summary; R = min{r in {16*2^k < T} U {T} : r >= m_max}
   if (tid == 0) {
-    const int mmax = s_mmax;
+    const int mmax = sh.mmax;
     int R = 0;
     if (n_active > 0) {
       R = T;
@@ -244,19 +297,26 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   }
 }
 
+template <int THREADS>
+hipError_t launch_threads(const int32_t* ids, const uint8_t* active, int T, int n_slots, int order, int32_t* seg,
+                          hipStream_t st) {
+  const size_t lds = 3 * (size_t)(n_slots > 0 ? n_slots : 1) * sizeof(int);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(build_segments_kernel<THREADS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(build_segments_kernel<THREADS>, dim3(1), dim3(THREADS), lds, st, ids, active, T, n_slots,
+                     order, seg);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_build_segments(const int32_t* ids, const uint8_t* active, int T, int n_slots, int order,
                                  int32_t* seg, hipStream_t st) {
-  size_t lds = 3 * (size_t)n_slots * sizeof(int);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(build_segments_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(kThreads), lds, st, ids, active, T, n_slots, order,
-                     seg);
-  return hipGetLastError();
+  if (T <= 256) return launch_threads<256>(ids, active, T, n_slots, order, seg, st);
+  return launch_threads<1024>(ids, active, T, n_slots, order, seg, st);
 }
 
 }  // namespace lora

@@ -2,24 +2,29 @@
 // adapter segment ("LoRazor" 3.1.1 Eq. 1; "LoRAForge" 5, rank-aware shrink:
 // directions beyond the adapter's retained rank exit before reading operands).
 //
-// Decode-sized work is a gather of A rows and is bound by HBM: each work
-// item is (row tile of <= 16 rows of one segment, block of 4 rank directions).
-// The 4 waves of the workgroup split d_in; every lane streams 16-byte chunks
-// of the 4 A rows and of the tile's x rows, so each A row is read from HBM
-// once per row tile (once per segment for segments of <= 16 rows) and x rows
-// come from L2.  Partial dot products are combined with a transposed
-// butterfly inside the wave (each shuffle step halves the values per lane)
-// and then across the 4 waves through LDS in a fixed order: no atomics, so
-// results are bitwise reproducible.
+// bf16 pools: one work item is (row tile of <= 16 rows of one segment, block
+// of 16 rank directions), computed as a 16 x 16 tile of MFMA
+// v_mfma_f32_16x16x32_bf16 products.  Operand fragments come straight from
+// global memory: lane l reads 16 contiguous bytes of token row (l mod 16)
+// and 16 contiguous bytes of direction row (l mod 16), at k offset
+// 8 * (l / 16) inside each 32-wide k chunk, so both operands stream in
+// 128-bit loads and A_a is read once per row tile.  The 16 waves of the
+// workgroup take interleaved k chunks (so that for decode widths every load
+// of a wave is in flight at once) and their 16 x 16 partial tiles are summed
+// through LDS in a fixed order: no atomics, bitwise reproducible.
+//
+// fp32 pools use the same tiling with v_mfma_f32_16x16x4f32 (four MFMAs per
+// 16-byte load, one per element).
 #include "common.h"
 #include "tiles.h"
+
+#include <algorithm>
 
 namespace lora {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kJB = 4;            // rank directions per workgroup
-
+constexpr int kThreads = 1024;        // 16 waves: for d_in <= 4096 a wave's loads all go out at once
+constexpr int kWaves = kThreads / 64;
 struct ShrinkArgs {
   const void* x;
   const void* A;
@@ -30,107 +35,40 @@ struct ShrinkArgs {
   int mode, nrb, rtiles, n_items;  // n_items: host item count (EXACT/BUCKETED/FULL)
 };
 
+constexpr int kDB = 16;           // rank directions per work item
+constexpr int kUnroll = 8;        // k chunks in flight per wave
+
+// One k chunk of the 16 x 16 tile: bf16 takes one 16x16x32 MFMA; fp32 takes
+// four 16x16x4 MFMAs, MFMA e using element e of every lane's 4 values, so
+// that the four lane groups x four elements cover the chunk's 16 k.
 template <typename TI>
-__device__ __forceinline__ float dot16(const u32x4_t& a, const u32x4_t& b, float acc);
-
-template <>
-__device__ __forceinline__ float dot16<uint16_t>(const u32x4_t& a, const u32x4_t& b, float acc) {
-  // exact widening of both bf16 halves, fp32 FMA
+__device__ __forceinline__ f32x4_t mfma_chunk(const u32x4_t& xv, const u32x4_t& av, f32x4_t acc) {
+  if constexpr (sizeof(TI) == 2) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv), __builtin_bit_cast(bf16x8_t, av),
+                                                   acc, 0, 0, 0);
+  } else {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc = fmaf(bf16lo(a[q]), bf16lo(b[q]), acc);
-    acc = fmaf(bf16hi(a[q]), bf16hi(b[q]), acc);
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xv[e]), __uint_as_float(av[e]), acc, 0, 0, 0);
+    return acc;
   }
-  return acc;
-}
-
-template <>
-__device__ __forceinline__ float dot16<float>(const u32x4_t& a, const u32x4_t& b, float acc) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(a[q]), __uint_as_float(b[q]), acc);
-  return acc;
-}
-
-// Sum NV per-lane values over the 64 lanes.  Afterwards lane l holds the
-// total of value index l >> (6 - log2 NV).
-template <int NV>
-__device__ __forceinline__ float wave_reduce_transpose(float (&v)[NV], int lane) {
-  constexpr int LOG2 = NV == 1 ? 0 : NV == 2 ? 1 : NV == 4 ? 2 : NV == 8 ? 3 : NV == 16 ? 4 : NV == 32 ? 5 : 6;
-  static_assert((1 << LOG2) == NV, "NV must be a power of two <= 64");
-#pragma unroll
-  for (int step = 0; step < LOG2; ++step) {
-    const int o = 32 >> step;
-    const int half = NV >> (step + 1);
-    const bool upper = (lane & o) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, o, 64);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int o = 32 >> LOG2; o >= 1; o >>= 1) r += __shfl_xor(r, o, 64);
-  return r;
-}
-
-template <typename TI, int MR>
-__device__ __forceinline__ void shrink_tile(const ShrinkArgs& a, const SegPtrs& P, const TileWork& w, int adapter,
-                                            int j0, int jn, float (*red)[64]) {
-  constexpr int VEC = 16 / sizeof(TI);
-  constexpr int NV = MR * kJB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const TI* __restrict__ X = static_cast<const TI*>(a.x);
-  const TI* __restrict__ Ab = static_cast<const TI*>(a.A);
-
-  const TI* xr[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) xr[m] = X + (size_t)P.perm[w.p0 + min(m, w.rows - 1)] * a.ld_x;
-  const TI* ar[kJB];
-#pragma unroll
-  for (int jj = 0; jj < kJB; ++jj) ar[jj] = Ab + ((size_t)adapter * a.r_cap + j0 + min(jj, jn - 1)) * a.d_in;
-
-  float acc[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-
-  const int stride = 4 * 64 * VEC;
-#pragma unroll 2
-  for (int k = (wave * 64 + lane) * VEC; k < a.d_in; k += stride) {
-    u32x4_t av[kJB];
-#pragma unroll
-    for (int jj = 0; jj < kJB; ++jj) av[jj] = jj < jn ? ld128(ar[jj] + k) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      if (m < w.rows) {
-        const u32x4_t xv = ld128(xr[m] + k);
-#pragma unroll
-        for (int jj = 0; jj < kJB; ++jj) acc[m * kJB + jj] = dot16<TI>(xv, av[jj], acc[m * kJB + jj]);
-      }
-    }
-  }
-
-  const float r = wave_reduce_transpose<NV>(acc, lane);
-  constexpr int GROUP = 64 / NV;
-  if ((lane & (GROUP - 1)) == 0) red[wave][lane / GROUP] = r;
-  __syncthreads();
-  if (threadIdx.x < NV) {
-    const int t = threadIdx.x;
-    const float s = red[0][t] + red[1][t] + red[2][t] + red[3][t];
-    const int m = t / kJB, jj = t - m * kJB;
-    if (m < w.rows && jj < jn) a.v[(size_t)(w.p0 + m) * a.ld_v + j0 + jj] = s;
-  }
-  __syncthreads();
 }
 
 template <typename TI>
-__global__ __launch_bounds__(kThreads) void shrink_gather_kernel(ShrinkArgs a) {
-  __shared__ float red[4][64];
+__global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
+  constexpr int VEC = 16 / sizeof(TI);      // elements per 16-byte load
+  constexpr int KC = 4 * VEC;               // k per chunk (4 lane groups)
+  __shared__ f32x4_t red[kWaves][64];
   const SegPtrs P = seg_ptrs(a.seg, a.T);
   if (!seg_valid(P, a.T)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int frow = lane & 15, fk = lane >> 4;
+  const TI* __restrict__ X = static_cast<const TI*>(a.x);
+  const TI* __restrict__ Ab = static_cast<const TI*>(a.A);
   int n_items = a.n_items;
   if (a.mode == LORA_LAUNCH_PERSISTENT) n_items = device_tile_count<LORA_TILE_SMALL>(P) * a.nrb;
+  const int nchunk = (a.d_in + KC - 1) / KC;
+
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int tile_item = item / a.nrb;
     const int rb = item - tile_item * a.nrb;
@@ -138,14 +76,39 @@ __global__ __launch_bounds__(kThreads) void shrink_gather_kernel(ShrinkArgs a) {
     if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, a.rtiles, w)) continue;
     const int adapter = P.seg_adapter[w.seg];
     const int r = a.slot_rank[adapter];
-    const int j0 = rb * kJB;
+    const int j0 = rb * kDB;
     if (j0 >= r) continue;                      // directions beyond the retained rank
-    const int jn = min(kJB, r - j0);
-    if (w.rows <= 1)      shrink_tile<TI, 1>(a, P, w, adapter, j0, jn, red);
-    else if (w.rows <= 2) shrink_tile<TI, 2>(a, P, w, adapter, j0, jn, red);
-    else if (w.rows <= 4) shrink_tile<TI, 4>(a, P, w, adapter, j0, jn, red);
-    else if (w.rows <= 8) shrink_tile<TI, 8>(a, P, w, adapter, j0, jn, red);
-    else                  shrink_tile<TI, 16>(a, P, w, adapter, j0, jn, red);
+    // rows past the tile and directions past the rank read a valid row; their
+    // results are never stored
+    const TI* xr = X + (size_t)P.perm[w.p0 + min(frow, w.rows - 1)] * a.ld_x + fk * VEC;
+    const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(frow, r - j0 - 1)) * a.d_in + fk * VEC;
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = wave; c0 < nchunk; c0 += kWaves * kUnroll) {
+      u32x4_t xv[kUnroll], av[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int k = (c0 + kWaves * u) * KC + fk * VEC;
+        const bool in = k < a.d_in;           // d_in % 8 == 0: a lane's group is all in or all out
+        xv[u] = in ? ld128(xr + (size_t)(c0 + kWaves * u) * KC) : u32x4_t{0, 0, 0, 0};
+        av[u] = in ? ld128(ar + (size_t)(c0 + kWaves * u) * KC) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc = mfma_chunk<TI>(xv[u], av[u], acc);
+    }
+    // acc[e] = partial v[row = 4 * (lane / 16) + e][direction = lane % 16]
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int t = threadIdx.x;              // one output each, waves summed in order
+      const int row = t >> 4, col = t & 15;
+      const int src = (row >> 2) * 16 + col, e = row & 3;
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) s += red[q][src][e];
+      if (row < w.rows && j0 + col < r) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + col] = s;
+    }
+    __syncthreads();
   }
 }
 
@@ -165,21 +128,23 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   a.T = T;
   a.ld_v = ld_v;
   a.mode = ls.mode;
-  a.nrb = (pool.r_cap + kJB - 1) / kJB;
+  a.nrb = (pool.r_cap + kDB - 1) / kDB;
   a.rtiles = host_row_tiles(ls, T, LORA_TILE_SMALL);
   int grid;
   if (ls.mode == LORA_LAUNCH_PERSISTENT) {
     a.n_items = 0;
-    grid = 2048;
+    // upper bound of the device tile count: sum_a ceil(m_a / 16) <= T / 16 + min(T, n_slots)
+    const long bound = ((long)T / LORA_TILE_SMALL + std::min(T, pool.n_slots)) * a.nrb;
+    grid = (int)std::min<long>(bound, 1024);
   } else {
     a.n_items = host_tile_items(ls, T, LORA_TILE_SMALL) * a.nrb;
     grid = a.n_items;
   }
   if (grid <= 0 || T == 0) return hipSuccess;
   if (pool.dtype == LORA_BF16)
-    hipLaunchKernelGGL(shrink_gather_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(shrink_mfma_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(shrink_gather_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(shrink_mfma_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -111,9 +111,8 @@ def main():
             c["pool"] = agm.pool_desc(c["A"], c["B"], c["rank"], c["scale"])
             c["base"] = agm.base_desc(c["W"], c["ws"])
             p = c["p"]
-            c["wsp"] = None
-            if flags:
-                c["wsp"] = torch.empty(agm.fused_workspace_bytes(T, p.d_in, flags), dtype=torch.uint8, device=dev)
+            bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p.base_dtype]
+            c["wsp"] = agm.fused_workspace(T, p.d_in, p.d_out, bt, flags, device=dev)
             inst.append(c)
         seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=dev)
         insts.append((inst, seg, ids.clone(), act.clone()))

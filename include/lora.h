@@ -203,9 +203,10 @@ int lora_build_segments_dev(const int32_t* ids, const uint8_t* active, int32_t T
  *   v      device fp32 [T, ld_v], ld_v >= r_cap
  *   summary  host summary of the segment build, or NULL when `launch` is
  *            LORA_LAUNCH_PERSISTENT or LORA_LAUNCH_FULL_BATCH
- * Decode-sized groups run a gather kernel (wave-wide dot products); groups of
- * more than LORA_TILE_SMALL rows run an MFMA-tiled kernel.  Deterministic:
- * fixed-order reductions, no atomics.
+ * Work items are (row tile of <= LORA_TILE_SMALL rows of one segment, block
+ * of 16 rank directions), each a 16 x 16 MFMA tile with operands streamed
+ * from global memory; blocks past the adapter's rank do no work.
+ * Deterministic: fixed-order reductions, no atomics.
  */
 int lora_shrink(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lora_summary_t* summary,
                 const void* x, int32_t ld_x, float* v, int32_t ld_v, int32_t launch, void* stream);
@@ -234,16 +235,25 @@ int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
  *            token into the workspace, fp8 MFMA).
  *   pool, v  NULL, NULL for the base product alone (seg may then be NULL:
  *            rows in batch order).
- *   workspace / workspace_bytes: device scratch of at least
- *            lora_fused_workspace_bytes(T, d_in, flags) bytes (0 unless W8A8).
- * y must not alias x.  Each output element is written exactly once.
+ *   workspace / workspace_bytes: device scratch, 256-byte aligned, of at
+ *            least lora_fused_workspace_bytes(T, d_in, d_out, base->dtype,
+ *            flags) bytes (NULL and 0 when that is 0).  It holds the W8A8
+ *            codes and scales, and for batches whose output has too few
+ *            tiles to fill the GPU the partial tiles of a split-k schedule
+ *            with one counter per tile; the call leaves the counters at zero.
+ *            Calls that share a workspace must be ordered on one stream.
+ *            LORA_E_SIZE if it is missing or too small.
+ * y must not alias x.  Results do not depend on the schedule's timing: split
+ * partial tiles are added in a fixed order.
  */
 int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
                       const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,
                       int32_t d_in, int32_t d_out, int32_t flags, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t flags);
+/* Workspace bytes lora_fused_linear needs for this call shape (with or
+ * without an adapter pool; the size with a pool covers both). */
+size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags);
 
 /*
  * Per-token activation quantisation for the W8A8 base product ("EpiLoRA" 2

@@ -199,5 +199,9 @@ def test_quant_and_dev_builder_validation():
     assert lib.lora_build_segments_dev(FAKE, None, 8, agm.DEV_MAX_SLOTS + 1, 0, FAKE, None) == agm.LORA_E_SIZE
     assert lib.lora_build_segments_dev(FAKE, None, 8, 4, 3, FAKE, None) == agm.LORA_E_ARG
     assert lib.lora_build_segments_dev(None, None, 8, 4, 0, FAKE, None) == agm.LORA_E_ARG
-    assert lib.lora_fused_workspace_bytes(4, 64, 0) == 0
-    assert lib.lora_fused_workspace_bytes(4, 64, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16
+    # bf16 with enough output tiles: no workspace; fp8 W8A8: codes + scales
+    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 0
+    assert lib.lora_fused_workspace_bytes(4, 64, 64, agm.FP8_E4M3, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16
+    # a small output (10 tiles of 64 x 64): 2 k splits + 1 adapter split per tile
+    assert lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0) == 10 * 3 * 64 * 64 * 4 + 10 * 4
+    assert lib.lora_fused_workspace_bytes(0, 64, 64, agm.BF16, 0) == 0
