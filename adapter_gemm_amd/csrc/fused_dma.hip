@@ -173,8 +173,7 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
   static_assert(STAGES >= 2, "the ring needs two slots");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
-  __shared__ int g_ad[BM], g_rank[BM], g_row0[BM], g_row1[BM], t_rowseg[BM];
-  __shared__ float g_scale[BM];
+  __shared__ int g_row0[BM], g_row1[BM], t_rowseg[BM];
   __shared__ int s_flag, s_sums[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -394,26 +393,48 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
       int n_chunks;
       const int w8 = (grk + 7) / 8;
       const int off = block_exclusive_sum(w8, s_sums, &n_chunks);
-      const int cm_off = BM * a.r_cap * 4;
-      uint16_t* cm = reinterpret_cast<uint16_t*>(ring + cm_off);
-      const int bsl_off = (cm_off + BM * a.r_cap / 4 + 1023) & ~1023;
+      // per packed chunk one record: x = group | j8 << 8 | lim << 12 |
+      // adapter << 16 (lim = ranks of the chunk below the group's rank, 1..8),
+      // y = the group's scale; per half step (4 chunks) the tile-local row
+      // range of its groups, r_lo | r_hi << 16
+      const int cap_chunks = BM * a.r_cap / 8;
+      uint2* crec = reinterpret_cast<uint2*>(ring + BM * a.r_cap * 4);
+      uint32_t* hrange = reinterpret_cast<uint32_t*>(crec + cap_chunks);
+      const int bsl_off = (BM * a.r_cap * 4 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
       uint8_t* bsl = ring + bsl_off;
       const int nb = min(kLoraNBMax, (RING - bsl_off) / BSLICE);   // >= 2 by the host plan
       if (tid < ng) {
-        g_ad[tid] = gad;
         g_row0[tid] = gr0;
         g_row1[tid] = gr1;
-        g_rank[tid] = grk;
-        g_scale[tid] = gsc;
-        for (int j = 0; j < w8; ++j) cm[off + j] = (uint16_t)((tid << 4) | j);
+        for (int j = 0; j < w8; ++j) {
+          const uint32_t lim = (uint32_t)min(8, grk - 8 * j);
+          crec[off + j] = make_uint2((uint32_t)tid | ((uint32_t)j << 8) | (lim << 12) | ((uint32_t)gad << 16),
+                                     __float_as_uint(gsc));
+        }
       }
       vm_drain();
+      lds_barrier();
+      const int nhalf = (n_chunks + 3) / 4;
+      for (int h = tid; h < nhalf; h += kThreads) {
+        const int lo = (int)(crec[4 * h].x & 0xff), hi = (int)(crec[min(4 * h + 3, n_chunks - 1)].x & 0xff);
+        hrange[h] = (uint32_t)g_row0[lo] | ((uint32_t)g_row1[hi] << 16);
+      }
+      // this lane's rows: group, v row offset and chunk rotation, per fragment
+      int rg[TM], vro[TM], vsh[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 16 + frow;
+        const int sg = t_rowseg[r];
+        rg[i] = sg < 0 ? -1 : sg - s_first;
+        vro[i] = r * a.r_cap;
+        vsh[i] = (r / vd) % rq;
+      }
       lds_barrier();
       const int nls = (n_chunks + 7) / 8;
       const i32x4_t brs = rsrc(a.B, a.b_bytes);
 
-      auto issue_b = [&](int t) {
-        uint8_t* dst = bsl + (t % nb) * BSLICE;
+      auto issue_b = [&](int t, int slot) {
+        uint8_t* dst = bsl + slot * BSLICE;
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
           const int s = (wave * LB + q) * 64 + lane;
@@ -421,38 +442,40 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
           const int kc = t * 8 + c;
           uint32_t o = kOOB;
           if (kc < n_chunks && n0 + n < a.d_out) {
-            const int e = cm[kc], g = e >> 4, j8 = e & 15;
-            o = (uint32_t)((((size_t)g_ad[g] * a.d_out + n0 + n) * a.r_cap + j8 * 8) * 2);
+            const uint32_t x = crec[kc].x;
+            o = (uint32_t)((((size_t)(x >> 16) * a.d_out + n0 + n) * a.r_cap + ((x >> 8) & 15) * 8) * 2);
           }
           dma16(brs, dst + (wave * LB + q) * 1024, o, 0u);
         }
       };
 
       const float* V = reinterpret_cast<const float*>(ring);
-      for (int t = 0; t < nb - 1 && t < nls; ++t) issue_b(t);
+      int slot = 0, fill = 0;
+      for (int t = 0; t < nb - 1 && t < nls; ++t) {
+        issue_b(t, fill);
+        fill = fill + 1 == nb ? 0 : fill + 1;
+      }
       for (int t = 0; t < nls; ++t) {
         wait_step<LB, kLoraNBMax - 2>(min(nb - 2, nls - 1 - t));
-        if (t + nb - 1 < nls) issue_b(t + nb - 1);
-        const uint8_t* Bs = bsl + (t % nb) * BSLICE;
+        if (t + nb - 1 < nls) {
+          issue_b(t + nb - 1, fill);
+          fill = fill + 1 == nb ? 0 : fill + 1;
+        }
+        const uint8_t* Bs = bsl + slot * BSLICE;
+        slot = slot + 1 == nb ? 0 : slot + 1;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+          const int h = 2 * t + kk;
+          if (h >= nhalf) break;
           // the groups of this half step are consecutive, so their rows are
           // one range [r_lo, r_hi); fragments outside it multiply zeros
-          const int kc_lo = t * 8 + kk * 4;
-          if (kc_lo >= n_chunks) break;
-          const int kc_hi = min(kc_lo + 3, n_chunks - 1);
-          const int r_lo = g_row0[cm[kc_lo] >> 4], r_hi = g_row1[cm[kc_hi] >> 4];
-          const int kc = kc_lo + fk;            // this lane's packed chunk
-          int g = -1, j8 = 0, rk = 0;
-          float sc = 0.f;
-          if (kc < n_chunks) {
-            const int e = cm[kc];
-            g = e >> 4;
-            j8 = e & 15;
-            rk = g_rank[g];
-            sc = g_scale[g];
-          }
-          const int lim = rk - j8 * 8;          // ranks of this chunk below the group's rank
+          const uint32_t hr = hrange[h];
+          const int r_lo = (int)(hr & 0xffff), r_hi = (int)(hr >> 16);
+          const int kc = 4 * h + fk;            // this lane's packed chunk
+          uint2 rec = make_uint2(0u, 0u);
+          if (kc < n_chunks) rec = crec[kc];
+          const int g = (int)(rec.x & 0xff), j8 = (int)((rec.x >> 8) & 15), lim = (int)((rec.x >> 12) & 15);
+          const float sc = __uint_as_float(rec.y);
           bf16x8_t fb[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
@@ -471,13 +494,13 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
           for (int i = 0; i < TM; ++i) {
             const int f0 = wm * WM + i * 16;
             if (f0 + 16 <= r_lo || f0 >= r_hi) continue;
-            const int r = f0 + frow;
             u32x4_t ua = {0, 0, 0, 0};
-            if (g >= 0 && t_rowseg[r] - s_first == g) {
-              const float* vr = V + r * a.r_cap;
-              const int sh = r / vd;
-              const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vr + ((2 * j8 + sh) % rq) * 4);
-              const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vr + ((2 * j8 + 1 + sh) % rq) * 4);
+            if (lim > 0 && rg[i] == g) {
+              int c0 = 2 * j8 + vsh[i];
+              if (c0 >= rq) c0 -= rq;
+              const int c1 = c0 + 1 == rq ? 0 : c0 + 1;
+              const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(V + vro[i] + c0 * 4);
+              const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(V + vro[i] + c1 * 4);
               float w[8];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -586,7 +609,8 @@ namespace {
 int ring_bytes(int bm, int bn, bool w8a16, int stages) { return stages * (bm * 128 + bn * (w8a16 ? 64 : 128)); }
 bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap) {
   if (r_cap <= 0) return true;
-  const int used = (bm * r_cap * 4 + bm * r_cap / 4 + 1023) & ~1023;
+  const int cap_chunks = bm * r_cap / 8;
+  const int used = (bm * r_cap * 4 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
   return ring_bytes(bm, bn, w8a16, stages) - used >= 2 * bn * 128;
 }
 }  // namespace
@@ -650,6 +674,7 @@ bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, i
   const long wb = (long)d_out * ld_w * (base_dtype == LORA_BF16 ? 2 : 1);
   if (xb > lim || wb > lim) return false;
   if (pool && (long)pool->n_slots * pool->d_out * pool->r_cap * 2 > lim) return false;
+  if (pool && pool->n_slots > 65535) return false;   // slot ids travel in 16 bits of the chunk records
   return true;
 }
 

@@ -43,11 +43,92 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "workload into profiles/ and exit")
+    ap.add_argument("--counter-command", default="", help="the command lines that produced the CSVs")
     return ap.parse_args()
+
+
+# Kernel whose roofline the bench line reports, and the sources it is built from
+# (a stored counter reading applies only while these are unchanged).
+DOMINANT = "fused_dma_kernel"
+DOMINANT_SOURCES = ["adapter_gemm_amd/csrc/fused_dma.hip", "adapter_gemm_amd/csrc/common.h"]
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DOMINANT_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{DOMINANT}_{workload}_traffic.txt")
+
+
+def summarise_counters(fetch_csv: str, write_csv: str, workload: str, copy_mb: int, command: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel,
+    scaled by what the same counter reads for the calibration copy of
+    copy_mb MiB (read once and written once)."""
+    import csv
+
+    def read(path, counter):
+        rows = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    copy_kib = copy_mb * 1024.0
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = read(path, counter)
+        kern = [v for n, v in rows if DOMINANT in n]
+        copies = [v for n, v in rows if "copy" in n.lower() and v >= 0.5 * copy_kib]
+        if not kern or not copies:
+            raise SystemExit(f"{path}: no {DOMINANT} or calibration-copy dispatches with {counter}")
+        factor = copy_kib / (sum(copies) / len(copies))
+        out[counter] = (sum(kern) / len(kern), factor, len(kern), len(copies))
+    fetch_kib, ff, nk, nc = out["FETCH_SIZE"]
+    write_kib, wf, _, _ = out["WRITE_SIZE"]
+    traffic = (fetch_kib * ff + write_kib * wf) * 1024.0
+    with open(traffic_file(workload), "w") as fh:
+        fh.write(f"# HBM traffic of {DOMINANT}, workload {workload} (rocprofv3 --pmc, one counter per run)\n")
+        fh.write(f"# commands: {command}\n")
+        fh.write(f"source_sha256 = {sources_digest()}\n")
+        fh.write(f"dispatches = {nk}\ncalibration_copy_mib = {copy_mb} ({nc} dispatches)\n")
+        fh.write(f"fetch_kib_per_dispatch = {fetch_kib:.1f}\nfetch_factor = {ff:.4f}\n")
+        fh.write(f"write_kib_per_dispatch = {write_kib:.1f}\nwrite_factor = {wf:.4f}\n")
+        fh.write(f"traffic_bytes_per_launch = {traffic:.0f}\n")
+    print(open(traffic_file(workload)).read())
+
+
+def stored_traffic(workload: str):
+    """Calibrated HBM bytes per launch of the dominant kernel, or None when no
+    reading exists or the kernel's sources changed since it was taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != sources_digest():
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
 
 
 def main():
     args = parse()
+    if args.counter_summary:
+        summarise_counters(args.counter_summary[0], args.counter_summary[1], args.config,
+                           args.calibrate_copy_mb or 256, args.counter_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU path is a design note, not an implementation.", file=sys.stderr)
@@ -144,25 +225,23 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # (1) whole-step throughput: K back-to-back steps between two events
+    # Timed region: K back-to-back steps between two events; events around
+    # every launch inside it give each kernel's own duration (all on the
+    # stream the library launches on: torch's current stream).
+    def mk(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    evs = [{"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_proj)} for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i, evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-
-    # (2) per-kernel durations: the same steps with events around each launch
-    def mk(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     per = {"seg": 0.0, "shrink": 0.0, "fused": 0.0}
-    for i in range(args.steps):
-        ev = {"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_proj)}
-        step(i, ev)
-        torch.cuda.synchronize()
+    for ev in evs:
         per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
         for j in range(n_proj):
             per["shrink"] += ev["shrink"][2 * j].elapsed_time(ev["shrink"][2 * j + 1])
@@ -211,10 +290,10 @@ def main():
         pk = MFMA_PEAK_TFLOPS[mfma_dtype]
         roof = {"bound": "mfma", "achieved": round(fused_tfs, 1), "peak": pk, "unit": "TFLOP/s",
                 "frac": round(fused_tfs / pk, 4)}
-    roof["kernel"] = "fused_gemm_kernel"
+    roof["kernel"] = DOMINANT
     roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_proj
     roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_proj
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(w.name)
 
     value = T / (ms_step * 1e-3)
     out = {

@@ -1,0 +1,108 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+bench.py times: device segment build (canonical order), persistent-mode
+shrink, fused linear with its planned workspace (fp8: W8A16, and W8A8 as an
+option).  Segments are compared in full, bit for bit; v and y on sampled rows
+against the fp64 oracle evaluated row by row on the same stored inputs.
+
+Tolerances (relative L2): v 1e-4; bf16 outputs 1e-2; fp8-base outputs 3e-2
+(the W8A8 option also within 1e-2 of the oracle's W8A8 definition).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():      # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import adapter_gemm_amd as agm
+import oracle
+from lora_inputs import make_workload
+from gpu_helpers import DEV, DevProjection, split_seg, rel_l2, row_rel_l2, to_f64
+
+TOL = {"fp32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
+N_SAMPLE = 64
+
+
+def _sample_rows(w, seed=7):
+    """64 rows at random plus, when present, rows that are not live and the
+    first and last row of the largest adapter group."""
+    g = np.random.default_rng(seed)
+    T = w.T
+    sel = set(g.choice(T, size=min(T, N_SAMPLE), replace=False).tolist())
+    live = oracle.live_rows(w.ids, w.active)
+    dead = np.flatnonzero(~live)
+    sel.update(dead[:4].tolist())
+    if live.any():
+        ids_live = w.ids[live]
+        big = np.bincount(ids_live).argmax()
+        rows = np.flatnonzero(live & (w.ids == big))
+        sel.update([int(rows[0]), int(rows[-1])])
+    return np.array(sorted(sel))
+
+
+def _run_path(w, dp, seg, flags=0):
+    p = dp.p
+    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+    agm.shrink(dp.pool, seg, w.T, None, dp.x, v, launch=agm.LAUNCH_PERSISTENT)
+    y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(dp.ydtype)
+    bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p.base_dtype]
+    ws = agm.fused_workspace(w.T, p.d_in, p.d_out, bt, flags, device=DEV)
+    agm.fused_linear(dp.base, dp.pool, seg, dp.x, v, y, flags=flags, workspace=ws)
+    torch.cuda.synchronize()
+    return v, y
+
+
+@pytest.mark.parametrize("name", ["tiny_sgmv", "decode_bgmv", "prefill_sgmv", "fp8_fused", "llama_layer"])
+def test_full_size_bench_path(name):
+    w = make_workload(name)
+    print(f"[full-size] {name}: T={w.T}, projections={len(w.projections)}", flush=True)
+    ids = torch.from_numpy(w.ids.astype(np.int32)).to(DEV)
+    act = torch.from_numpy(w.active.astype(np.uint8)).to(DEV)
+    N = w.projections[0].n_slots
+    seg = torch.empty(agm.segment_words(w.T), dtype=torch.int32, device=DEV)
+    agm.build_segments_dev(ids, act, N, seg)
+    torch.cuda.synchronize()
+    d = split_seg(seg, w.T)
+    ref = oracle.build_segments(w.ids, w.active, 0)
+    S = ref["S"]
+    assert int(d["sum"][7]) == 0 and int(d["sum"][0]) == ref["n_active"] and int(d["sum"][1]) == S
+    assert np.array_equal(d["perm"], ref["perm"])
+    assert np.array_equal(d["seg_start"][:S + 1], ref["seg_start"])
+    assert np.array_equal(d["seg_adapter"][:S], ref["seg_adapter"])
+
+    sel = _sample_rows(w)
+    pos_of_row = np.empty(w.T, np.int64)
+    pos_of_row[d["perm"]] = np.arange(w.T)
+    n_act = ref["n_active"]
+    for p in w.projections:
+        dp = DevProjection(w, p)
+        v, y = _run_path(w, dp, seg)
+        args = dp.oracle_args(w)
+        xs = dp.x_host[sel]
+        ids_s, act_s = w.ids[sel], w.active[sel]
+        y_ref = oracle.linear(xs, dp.w0_host, ids_s, act_s, *args[3:])
+        got = to_f64(y)[sel]
+        tol = TOL["fp8"] if p.base_dtype == "fp8" else TOL[p.data_dtype]
+        assert np.isfinite(got).all(), (name, p.name)
+        assert rel_l2(got, y_ref) <= tol, (name, p.name, rel_l2(got, y_ref))
+        assert row_rel_l2(got, y_ref) <= tol, (name, p.name, row_rel_l2(got, y_ref))
+        # v of the sampled live rows, at their grouped positions
+        live_s = oracle.live_rows(ids_s, act_s)
+        if live_s.any():
+            v_ref = oracle.shrink_rows(xs[live_s], ids_s[live_s], act_s[live_s], dp.A_host, p.slot_rank)
+            pos = pos_of_row[sel[live_s]]
+            assert (pos < n_act).all()
+            vg = v.cpu().numpy().astype(np.float64)[pos]
+            mask = np.arange(p.r_cap)[None, :] < p.slot_rank[ids_s[live_s]][:, None]
+            assert rel_l2(np.where(mask, vg, 0), v_ref) <= TOL["fp32"], (name, p.name)
+        if p.base_dtype == "fp8":
+            _, y8 = _run_path(w, dp, seg, flags=agm.FLAG_ACT_QUANT_E4M3)
+            got8 = to_f64(y8)[sel]
+            assert rel_l2(got8, y_ref) <= TOL["fp8"], (name, rel_l2(got8, y_ref))
+            ref8 = oracle.linear_w8a8(xs, dp.w0_host[0], dp.w0_host[1], ids_s, act_s, *args[3:])
+            assert rel_l2(got8, ref8) <= TOL["bf16"] and row_rel_l2(got8, ref8) <= TOL["bf16"]
+        print(f"[full-size] {name}/{p.name}: rel L2 {rel_l2(got, y_ref):.2e} on {len(sel)} rows", flush=True)
+        del dp, v, y
+        torch.cuda.empty_cache()
