@@ -4,7 +4,8 @@
 // whose epilogue adds, per adapter group in the output tile, h_l B_l^T over
 // the tile's slice of B_l, then writes rows back in token order).
 //
-// Main loop.  A workgroup (4 waves, 2 x 2) owns a BM x BN output tile.  Every
+// Main loop.  A workgroup (4 or 8 waves in a WGM x WGN grid) owns a BM x BN
+// output tile.  Every
 // k-step stages a BM x 128-byte slab of x rows (gathered through the grouped
 // order) and a BN x 128-byte (bf16, W8A8) or BN x 64-byte (fp8 codes, W8A16)
 // slab of W0 rows in one slot of an LDS ring of STAGES slots.  The slabs are
@@ -38,7 +39,6 @@
 namespace lora {
 namespace {
 
-constexpr int kThreads = 256;
 enum DmaMode { kBF16 = 0, kW8A16 = 1, kW8A8 = 2 };
 constexpr uint32_t kOOB = 0x80000000u;   // offset past every descriptor's range: loads return zeros
 constexpr int kLoraNBMax = 4;            // adapter-phase ring slots (at most)
@@ -122,7 +122,8 @@ __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // memory operations may stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
+// Exclusive prefix sum over the NW waves of the workgroup; *total gets the sum.
+template <int NW>
 __device__ __forceinline__ int block_exclusive_sum(int v, int* sums, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -133,9 +134,13 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* sums, int* total)
   }
   if (lane == 63) sums[wave] = incl;
   lds_barrier();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += sums[w];
-  *total = sums[0] + sums[1] + sums[2] + sums[3];
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) before += sums[w];
+    all += sums[w];
+  }
+  *total = all;
   lds_barrier();
   return before + incl - v;
 }
@@ -157,27 +162,30 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 c) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-template <int BM, int BN, int MODE, int STAGES>
-__global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
+  constexpr int NW = WGM * WGN, NT = 64 * NW;          // waves (WGM x WGN grid) and threads
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int WROW = MODE == kW8A16 ? 64 : 128;      // W bytes per row per k-step
   constexpr int XS = BM * 128, WSB = BN * WROW, STAGE = XS + WSB;
-  constexpr int LX = XS / 4096, LW = WSB / 4096, L = LX + LW;   // DMA ops per wave per step
+  constexpr int LX = XS / (1024 * NW), LW = WSB / (1024 * NW), L = LX + LW;   // DMA ops per wave per step
   constexpr int RING = STAGES * STAGE;
   constexpr int BSLICE = BN * 128;                     // one adapter step: BN channels x 64 packed ranks
-  constexpr int LB = BSLICE / 4096;
+  constexpr int LB = BSLICE / (1024 * NW);
   constexpr int XE = MODE == kW8A8 ? 1 : 2;            // x element bytes
   constexpr int WE = MODE == kBF16 ? 2 : 1;            // W element bytes
-  static_assert(XS % 4096 == 0 && WSB % 4096 == 0, "slabs must be whole 1 KB DMA rows per wave");
+  static_assert(XS % (1024 * NW) == 0 && WSB % (1024 * NW) == 0 && BSLICE % (1024 * NW) == 0,
+                "slabs must be whole 1 KB DMA rows per wave");
+  static_assert(NT >= BM && WM % 16 == 0 && WN % 16 == 0, "one thread per tile row; 16 x 16 fragments");
   static_assert(STAGES >= 2, "the ring needs two slots");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
   __shared__ int g_row0[BM], g_row1[BM], t_rowseg[BM];
-  __shared__ int s_flag, s_sums[4];
+  __shared__ int s_flag, s_sums[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int frow = lane & 15, fk = lane >> 4;
 
   // ---- work item: (tile, split) ------------------------------------------
@@ -369,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
       const int vd = rq >= 16 ? 1 : 16 / rq;
       const int vchunks = BM * rq;              // a multiple of 128
       const i32x4_t vrs = rsrc(a.v, a.v_bytes);
-      for (int c0 = wave * 64; c0 < vchunks; c0 += 256) {
+      for (int c0 = wave * 64; c0 < vchunks; c0 += NT) {
         const int c = c0 + lane;
         const int row = c / rq, phys = c - row * rq;
         const int c4 = (phys + rq - (row / vd) % rq) % rq;
@@ -392,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
       }
       int n_chunks;
       const int w8 = (grk + 7) / 8;
-      const int off = block_exclusive_sum(w8, s_sums, &n_chunks);
+      const int off = block_exclusive_sum<NW>(w8, s_sums, &n_chunks);
       // per packed chunk one record: x = group | j8 << 8 | lim << 12 |
       // adapter << 16 (lim = ranks of the chunk below the group's rank, 1..8),
       // y = the group's scale; per half step (4 chunks) the tile-local row
@@ -415,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(DmaArgs a) {
       vm_drain();
       lds_barrier();
       const int nhalf = (n_chunks + 3) / 4;
-      for (int h = tid; h < nhalf; h += kThreads) {
+      for (int h = tid; h < nhalf; h += NT) {
         const int lo = (int)(crec[4 * h].x & 0xff), hi = (int)(crec[min(4 * h + 3, n_chunks - 1)].x & 0xff);
         hrange[h] = (uint32_t)g_row0[lo] | ((uint32_t)g_row1[hi] << 16);
       }
@@ -580,7 +588,7 @@ __global__ void zero_words_kernel(int32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-template <int BM, int BN, int MODE, int STAGES>
+template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN>
 hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
   const int S_total = a.splits + a.lora_split;
   if (S_total > 1) {
@@ -588,17 +596,25 @@ hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fused_dma_kernel<BM, BN, MODE, STAGES>), dim3(pl.tiles * S_total), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN>), dim3(pl.tiles * S_total),
+                     dim3(64 * WGM * WGN), 0, st, a);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
   if constexpr (MODE != kW8A16) {
-    if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3>(a, pl, st);
+    if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3, 4, 2>(a, pl, st);
   }
-  if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4>(a, pl, st);
-  return launch_cfg<64, 64, MODE, 4>(a, pl, st);
+  // 8 waves (two per SIMD) hide LDS and barrier latency; the wave grids are
+  // the measured best per tile (the 64 x 64 W8A16 slab is too small for 8)
+  if constexpr (MODE == kW8A16) {
+    if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4, 2, 4>(a, pl, st);
+    return launch_cfg<64, 64, MODE, 4, 2, 2>(a, pl, st);
+  } else {
+    if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4, 4, 2>(a, pl, st);
+    return launch_cfg<64, 64, MODE, 4, 2, 4>(a, pl, st);
+  }
 }
 
 }  // namespace

@@ -225,21 +225,28 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K back-to-back steps between two events; events around
-    # every launch inside it give each kernel's own duration (all on the
-    # stream the library launches on: torch's current stream).
-    def mk(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    evs = [{"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_proj)} for _ in range(args.steps)]
+    # Timed region: K back-to-back steps between two events (the line's value).
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
+
+    # The same K steps again with events around every launch, on the stream
+    # the library launches on (torch's current stream), for each kernel's own
+    # duration.  Event packets add gaps between launches, so the step time
+    # above comes from the run without them.
+    def mk(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    evs = [{"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_proj)} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     per = {"seg": 0.0, "shrink": 0.0, "fused": 0.0}
     for ev in evs:
         per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
