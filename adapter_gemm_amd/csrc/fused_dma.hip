@@ -181,7 +181,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   static_assert(STAGES >= 2, "the ring needs two slots");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
-  __shared__ int g_row0[BM], g_row1[BM], t_rowseg[BM];
+  __shared__ int g_row0[BM], g_row1[BM], g_rank[BM], t_rowseg[BM];
+  __shared__ float g_scale[BM];
   __shared__ int s_flag, s_sums[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -369,11 +370,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     const int pe = min(m0 + BM, n_active);
     if (m0 < pe) {
       vm_barrier<0>();                          // ring free: every wave is past its last main step
-      // raw fp32 v rows [m0, pe) x r_cap -> ring[0, BM * r_cap * 4); rows at
-      // or past pe read as zeros.  Logical 16-byte chunk c4 of row r sits at
-      // chunk (c4 + r / vd) mod rq of the row, so that the 16 rows a fragment
-      // read touches fall in distinct LDS banks.
-      const int rq = a.r_cap / 4;               // 16-byte chunks per v row
+      // LDS layout of the phase: [v16: bf16 s_g v, BM x c16 chunks][chunk
+      // records][half-step row ranges] | slot region: raw fp32 v during the
+      // set-up, then nb B slices of BSLICE bytes
+      const int c16 = a.r_cap / 8;              // 16-byte bf16 chunks per v row
+      const int cap_chunks = BM * c16;          // packed chunks at most (ng <= BM, ranks <= r_cap)
+      uint8_t* v16 = ring;
+      uint2* crec = reinterpret_cast<uint2*>(ring + BM * a.r_cap * 2);
+      uint32_t* hrange = reinterpret_cast<uint32_t*>(crec + cap_chunks);
+      const int slot_off = (BM * a.r_cap * 2 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
+      uint8_t* bsl = ring + slot_off;
+      const int nb = min(kLoraNBMax, (RING - slot_off) / BSLICE);   // >= 2 by the host plan
+
+      // raw fp32 v rows [m0, pe) x r_cap -> slot region; rows at or past pe
+      // read as zeros.  Logical 16-byte chunk c4 of row r sits at chunk
+      // (c4 + r / vd) mod rq of the row, so that a pass over one column of 16
+      // rows touches distinct LDS banks.
+      const int rq = a.r_cap / 4;
       const int vd = rq >= 16 ? 1 : 16 / rq;
       const int vchunks = BM * rq;              // a multiple of 128
       const i32x4_t vrs = rsrc(a.v, a.v_bytes);
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
         const int row = c / rq, phys = c - row * rq;
         const int c4 = (phys + rq - (row / vd) % rq) % rq;
         const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
-        dma16(vrs, ring + c0 * 16, o, 0u);
+        dma16(vrs, bsl + c0 * 16, o, 0u);
       }
       // group table (segments meeting the tile's live rows)
       if (tid < BM) t_rowseg[tid] = my_rowseg;
@@ -401,45 +414,69 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
       int n_chunks;
       const int w8 = (grk + 7) / 8;
       const int off = block_exclusive_sum<NW>(w8, s_sums, &n_chunks);
-      // per packed chunk one record: x = group | j8 << 8 | lim << 12 |
-      // adapter << 16 (lim = ranks of the chunk below the group's rank, 1..8),
-      // y = the group's scale; per half step (4 chunks) the tile-local row
-      // range of its groups, r_lo | r_hi << 16
-      const int cap_chunks = BM * a.r_cap / 8;
-      uint2* crec = reinterpret_cast<uint2*>(ring + BM * a.r_cap * 4);
-      uint32_t* hrange = reinterpret_cast<uint32_t*>(crec + cap_chunks);
-      const int bsl_off = (BM * a.r_cap * 4 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
-      uint8_t* bsl = ring + bsl_off;
-      const int nb = min(kLoraNBMax, (RING - bsl_off) / BSLICE);   // >= 2 by the host plan
+      // per packed chunk: x = group | j8 << 8 | lim << 12 (lim = ranks of the
+      // chunk below the group's rank, 1..8), y = byte offset of the chunk's 8
+      // ranks of channel 0 of B_g; per group its rank and scale for the v tile
       if (tid < ng) {
         g_row0[tid] = gr0;
         g_row1[tid] = gr1;
+        g_rank[tid] = grk;
+        g_scale[tid] = gsc;
         for (int j = 0; j < w8; ++j) {
           const uint32_t lim = (uint32_t)min(8, grk - 8 * j);
-          crec[off + j] = make_uint2((uint32_t)tid | ((uint32_t)j << 8) | (lim << 12) | ((uint32_t)gad << 16),
-                                     __float_as_uint(gsc));
+          crec[off + j] = make_uint2((uint32_t)tid | ((uint32_t)j << 8) | (lim << 12),
+                                     (uint32_t)((size_t)gad * a.d_out * a.r_cap * 2 + j * 16));
         }
       }
-      vm_drain();
+      vm_drain();                               // the raw v rows have landed
       lds_barrier();
+      // v16[row] = bf16(s_g v[row, j]) for j < r_g of the row's group, else 0;
+      // chunk j8 of row r at (j8 + r / vd16) mod c16
+      const int vd16 = c16 >= 16 ? 1 : 16 / c16;
+      const float* V32 = reinterpret_cast<const float*>(bsl);
+      for (int u = tid; u < BM * c16; u += NT) {
+        const int r = u / c16, j8 = u - r * c16;
+        const int sg = t_rowseg[r];
+        u32x4_t o = {0, 0, 0, 0};
+        if (sg >= 0) {
+          const int g = sg - s_first;
+          const int lim = g_rank[g] - 8 * j8;
+          if (lim > 0) {
+            const float sc = g_scale[g];
+            const int p0 = (2 * j8 + (r / vd) % rq) % rq, p1 = (2 * j8 + 1 + (r / vd) % rq) % rq;
+            const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(V32 + r * a.r_cap + p0 * 4);
+            const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(V32 + r * a.r_cap + p1 * 4);
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[e] = e < lim ? sc * a0[e] : 0.f;
+              w[4 + e] = 4 + e < lim ? sc * a1[e] : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
+          }
+        }
+        *reinterpret_cast<u32x4_t*>(v16 + (r * c16 + (j8 + r / vd16) % c16) * 16) = o;
+      }
       const int nhalf = (n_chunks + 3) / 4;
       for (int h = tid; h < nhalf; h += NT) {
         const int lo = (int)(crec[4 * h].x & 0xff), hi = (int)(crec[min(4 * h + 3, n_chunks - 1)].x & 0xff);
         hrange[h] = (uint32_t)g_row0[lo] | ((uint32_t)g_row1[hi] << 16);
       }
-      // this lane's rows: group, v row offset and chunk rotation, per fragment
+      // this lane's rows: group, v16 row offset and chunk rotation, per fragment
       int rg[TM], vro[TM], vsh[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WM + i * 16 + frow;
         const int sg = t_rowseg[r];
         rg[i] = sg < 0 ? -1 : sg - s_first;
-        vro[i] = r * a.r_cap;
-        vsh[i] = (r / vd) % rq;
+        vro[i] = r * c16;
+        vsh[i] = (r / vd16) % c16;
       }
-      lds_barrier();
+      lds_barrier();                            // v16, ranges ready; the slot region is free
       const int nls = (n_chunks + 7) / 8;
       const i32x4_t brs = rsrc(a.B, a.b_bytes);
+      const uint32_t nrow_bytes = (uint32_t)a.r_cap * 2;
 
       auto issue_b = [&](int t, int slot) {
         uint8_t* dst = bsl + slot * BSLICE;
@@ -449,15 +486,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           const int n = s >> 3, c = (s & 7) ^ (n & 7);
           const int kc = t * 8 + c;
           uint32_t o = kOOB;
-          if (kc < n_chunks && n0 + n < a.d_out) {
-            const uint32_t x = crec[kc].x;
-            o = (uint32_t)((((size_t)(x >> 16) * a.d_out + n0 + n) * a.r_cap + ((x >> 8) & 15) * 8) * 2);
-          }
+          if (kc < n_chunks && n0 + n < a.d_out) o = crec[kc].y + (uint32_t)(n0 + n) * nrow_bytes;
           dma16(brs, dst + (wave * LB + q) * 1024, o, 0u);
         }
       };
 
-      const float* V = reinterpret_cast<const float*>(ring);
       int slot = 0, fill = 0;
       for (int t = 0; t < nb - 1 && t < nls; ++t) {
         issue_b(t, fill);
@@ -480,10 +513,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           const uint32_t hr = hrange[h];
           const int r_lo = (int)(hr & 0xffff), r_hi = (int)(hr >> 16);
           const int kc = 4 * h + fk;            // this lane's packed chunk
-          uint2 rec = make_uint2(0u, 0u);
-          if (kc < n_chunks) rec = crec[kc];
-          const int g = (int)(rec.x & 0xff), j8 = (int)((rec.x >> 8) & 15), lim = (int)((rec.x >> 12) & 15);
-          const float sc = __uint_as_float(rec.y);
+          const uint32_t rx = kc < n_chunks ? crec[kc].x : 0u;
+          const int g = kc < n_chunks ? (int)(rx & 0xff) : -2;
+          const int j8 = (int)((rx >> 8) & 15), lim = (int)((rx >> 12) & 15);
           bf16x8_t fb[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
@@ -502,22 +534,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           for (int i = 0; i < TM; ++i) {
             const int f0 = wm * WM + i * 16;
             if (f0 + 16 <= r_lo || f0 >= r_hi) continue;
-            u32x4_t ua = {0, 0, 0, 0};
-            if (lim > 0 && rg[i] == g) {
-              int c0 = 2 * j8 + vsh[i];
-              if (c0 >= rq) c0 -= rq;
-              const int c1 = c0 + 1 == rq ? 0 : c0 + 1;
-              const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(V + vro[i] + c0 * 4);
-              const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(V + vro[i] + c1 * 4);
-              float w[8];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                w[e] = e < lim ? sc * v0[e] : 0.f;
-                w[4 + e] = 4 + e < lim ? sc * v1[e] : 0.f;
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) ua[e] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
-            }
+            int cj = j8 + vsh[i];
+            if (cj >= c16) cj -= c16;
+            u32x4_t ua = *reinterpret_cast<const u32x4_t*>(v16 + (vro[i] + cj) * 16);
+            if (rg[i] != g) ua = u32x4_t{0, 0, 0, 0};
             const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, ua);
 #pragma unroll
             for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
@@ -626,8 +646,9 @@ int ring_bytes(int bm, int bn, bool w8a16, int stages) { return stages * (bm * 1
 bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap) {
   if (r_cap <= 0) return true;
   const int cap_chunks = bm * r_cap / 8;
-  const int used = (bm * r_cap * 4 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
-  return ring_bytes(bm, bn, w8a16, stages) - used >= 2 * bn * 128;
+  const int used = (bm * r_cap * 2 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
+  const int avail = ring_bytes(bm, bn, w8a16, stages) - used;
+  return avail >= 2 * bn * 128 && avail >= bm * r_cap * 4;   // two B slices; the raw v rows
 }
 }  // namespace
 
