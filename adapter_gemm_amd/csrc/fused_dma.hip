@@ -624,6 +624,7 @@ hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
 template <int MODE>
 hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
   if constexpr (MODE != kW8A16) {
+    if (pl.bm == 256 && pl.bn == 256) return launch_cfg<256, 256, MODE, 2, 4, 2>(a, pl, st);
     if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3, 4, 2>(a, pl, st);
   }
   // 8 waves (two per SIMD) hide LDS and barrier latency; the wave grids are
@@ -663,14 +664,15 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   if (d_in % kb) return pl;
   // the largest tile that still gives every CU a tile (>= 256 tiles), else
   // 64 x 64; 256-row tiles are not built for the widened-fp8 mode
-  struct Cfg { int bm, bn, stages; };
-  const Cfg cands[] = {{256, 128, 3}, {128, 128, 4}, {64, 64, 4}};
+  // (256 x 256 needs two full rounds of the chip to beat 256 x 128's balance)
+  struct Cfg { int bm, bn, stages, min_tiles; };
+  const Cfg cands[] = {{256, 256, 2, 512}, {256, 128, 3, 256}, {128, 128, 4, 256}, {64, 64, 4, 0}};
   const Cfg* pick = nullptr;
   for (const Cfg& c : cands) {
     if (c.bm == 256 && w8a16) continue;
     if (!lora_fits(c.bm, c.bn, w8a16, c.stages, r_cap)) continue;
     const long tiles = (long)((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
-    if (tiles >= 256 || c.bm == 64) { pick = &c; break; }
+    if (tiles >= c.min_tiles) { pick = &c; break; }
   }
   if (!pick) return pl;
   pl.dma = true;
