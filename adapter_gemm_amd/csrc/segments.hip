@@ -12,9 +12,11 @@
 //      id: every lane learns its rank among equal ids inside the wave, and one
 //      leader lane per distinct id adds the run length to an LDS histogram
 //      (for order = 1 it also records the first row of the id);
-//   2. segment index per adapter (exclusive scan of "present", or of first
-//      appearances over the rows), segment starts, row tiles of 16 and 64
-//      rows, m_max and R;
+//   2. segment index per adapter, segment starts, row tiles of 16 and 64
+//      rows, m_max and R.  Canonical order: one scan over the adapters of
+//      (present, rows, 16-row tiles, 64-row tiles) gives all of them and the
+//      placement cursors at once.  First-appearance order: a scan of first
+//      appearances over the rows, then a scan over the segments;
 //   3. the chunk's waves visit a per-adapter cursor in wave order: each
 //      leader takes its run's base position and advances the cursor, so rows
 //      land in batch order inside every segment (stable, deterministic) while
@@ -26,41 +28,66 @@ namespace {
 
 struct BuildLds {
   int wave_sums[17];
+  int4 wave_sums4[16];
   int err, nseg, nact, mmax, dead_run;
   int wave_dead[16];
   int run_base[16][64];     // per wave: base position of the run led by each lane
 };
 
-// exclusive scan of one value per thread over the workgroup; the total is
-// written to *total for every thread
+// Inclusive prefix sum over the 64 lanes of a wave: DPP shifts inside rows
+// of 16 lanes, then row broadcasts (lane 15 into rows 1 and 3, lane 31 into
+// rows 2 and 3).  Lanes whose DPP source is disabled add 0.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over the workgroup; the total
+// is written to *total for every thread.
 template <int THREADS>
 __device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
   constexpr int kWaves = THREADS / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_incl_sum(v);
   if (lane == 63) wave_sums[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    const int s = lane < kWaves ? wave_sums[lane] : 0;
-    int si = s;
+  int before = 0, all = 0;
 #pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const int t = __shfl_up(si, o, 64);
-      if (lane >= o) si += t;
-    }
-    if (lane < kWaves) wave_sums[lane] = si - s;
-    if (lane == kWaves - 1) wave_sums[kWaves] = si;
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = wave_sums[w];
+    if (w < wave) before += t;
+    all += t;
   }
+  *total = all;
   __syncthreads();
-  const int res = wave_sums[wave] + incl - v;
-  *total = wave_sums[kWaves];
+  return before + incl - v;
+}
+
+// Exclusive prefix sums of four values per thread over the workgroup, with
+// their totals (all threads).
+template <int THREADS>
+__device__ int4 block_exclusive_scan4(int4 v, int4* wave_sums, int4* total) {
+  constexpr int kWaves = THREADS / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int4 incl = make_int4(wave_incl_sum(v.x), wave_incl_sum(v.y), wave_incl_sum(v.z), wave_incl_sum(v.w));
+  if (lane == 63) wave_sums[wave] = incl;
   __syncthreads();
-  return res;
+  int4 before = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int4 t = wave_sums[w];
+    if (w < wave) { before.x += t.x; before.y += t.y; before.z += t.z; before.w += t.w; }
+    all.x += t.x; all.y += t.y; all.z += t.z; all.w += t.w;
+  }
+  *total = all;
+  __syncthreads();
+  return make_int4(before.x + incl.x - v.x, before.y + incl.y - v.y, before.z + incl.z - v.z,
+                   before.w + incl.w - v.w);
 }
 
 // Runs of equal live ids inside one wave.  Returns the lane's rank among the
@@ -83,6 +110,64 @@ __device__ __forceinline__ int wave_runs(bool live, int id, int lane, int& leade
     remaining &= ~m;
   }
   return rank;
+}
+
+// First-appearance order: segment lengths in segment order, then segment
+// starts, row tiles and the placement cursors (cnt[a] = start of a's
+// segment).  sh.nseg holds the segment count.
+template <int THREADS>
+__device__ void build_order1_segments(int N, int* cnt, const int* sidx, int* sst, const SegPtrs& P, BuildLds& sh) {
+  const int tid = threadIdx.x;
+  const int S = sh.nseg;
+  for (int a = tid; a < N; a += THREADS) {
+    if (cnt[a] > 0) {
+      sst[sidx[a]] = cnt[a];
+      P.seg_adapter[sidx[a]] = a;
+      atomicMax(&sh.mmax, cnt[a]);
+    }
+  }
+  __syncthreads();
+
+  // segment starts and row tiles
+  {
+    int run = 0, run_s = 0, run_l = 0;
+    for (int base = 0; base < S; base += THREADS) {
+      const int s = base + tid;
+      const int len = s < S ? sst[s] : 0;
+      const int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
+      const int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
+      int tot, tot_s, tot_l;
+      const int st = block_exclusive_scan<THREADS>(len, sh.wave_sums, &tot) + run;
+      const int os = block_exclusive_scan<THREADS>(ns, sh.wave_sums, &tot_s) + run_s;
+      const int ol = block_exclusive_scan<THREADS>(nl, sh.wave_sums, &tot_l) + run_l;
+      if (s < S) {
+        P.seg_start[s] = st;
+        for (int t = 0; t < ns; ++t) {
+          P.tiles_small[2 * (os + t)] = st + t * LORA_TILE_SMALL;
+          P.tiles_small[2 * (os + t) + 1] = s;
+        }
+        for (int t = 0; t < nl; ++t) {
+          P.tiles_large[2 * (ol + t)] = st + t * LORA_TILE_LARGE;
+          P.tiles_large[2 * (ol + t) + 1] = s;
+        }
+        sst[s] = st;
+      }
+      run += tot;
+      run_s += tot_s;
+      run_l += tot_l;
+    }
+    if (tid == 0) {
+      P.seg_start[S] = run;
+      sh.nact = run;
+      P.sum[kNTilesSmall] = run_s;
+      P.sum[kNTilesLarge] = run_l;
+    }
+  }
+  __syncthreads();
+
+  // placement cursor per adapter = start of its segment
+  for (int a = tid; a < N; a += THREADS)
+    if (cnt[a] > 0) cnt[a] = sst[sidx[a]];
 }
 
 template <int THREADS>
@@ -142,18 +227,43 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
     return;
   }
 
-  // 2. segment index of each present adapter
+  // 2. segments
   if (order == 0) {
-    int run = 0;
+    // adapters in ascending id: segment index, start and tile offsets are
+    // prefix sums over the adapters; cnt becomes the placement cursor
+    int4 run = make_int4(0, 0, 0, 0);
     for (int base = 0; base < N; base += THREADS) {
       const int a = base + tid;
-      const int present = (a < N && cnt[a] > 0) ? 1 : 0;
-      int tot;
-      const int ex = block_exclusive_scan<THREADS>(present, sh.wave_sums, &tot);
-      if (present) sidx[a] = run + ex;
-      run += tot;
+      const int len = a < N ? cnt[a] : 0;
+      const int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
+      const int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
+      int4 tot;
+      const int4 ex = block_exclusive_scan4<THREADS>(make_int4(len > 0, len, ns, nl), sh.wave_sums4, &tot);
+      if (len > 0) {
+        const int sg = run.x + ex.x, st = run.y + ex.y, os = run.z + ex.z, ol = run.w + ex.w;
+        sidx[a] = sg;
+        P.seg_adapter[sg] = a;
+        P.seg_start[sg] = st;
+        for (int t = 0; t < ns; ++t) {
+          P.tiles_small[2 * (os + t)] = st + t * LORA_TILE_SMALL;
+          P.tiles_small[2 * (os + t) + 1] = sg;
+        }
+        for (int t = 0; t < nl; ++t) {
+          P.tiles_large[2 * (ol + t)] = st + t * LORA_TILE_LARGE;
+          P.tiles_large[2 * (ol + t) + 1] = sg;
+        }
+        cnt[a] = st;
+        atomicMax(&sh.mmax, len);
+      }
+      run.x += tot.x; run.y += tot.y; run.z += tot.z; run.w += tot.w;
     }
-    if (tid == 0) sh.nseg = run;
+    if (tid == 0) {
+      sh.nseg = run.x;
+      sh.nact = run.y;
+      P.seg_start[run.x] = run.y;
+      P.sum[kNTilesSmall] = run.z;
+      P.sum[kNTilesLarge] = run.w;
+    }
   } else {
     // rows that are the first appearance of their adapter, in batch order;
     // indices are stored negated so that a later row never matches
@@ -175,60 +285,12 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
     for (int a = tid; a < N; a += THREADS)
       if (cnt[a] > 0) sidx[a] = -sidx[a] - 1;
     if (tid == 0) sh.nseg = run;
+    __syncthreads();
+    build_order1_segments<THREADS>(N, cnt, sidx, sst, P, sh);
   }
   __syncthreads();
   const int S = sh.nseg;
 
-  for (int a = tid; a < N; a += THREADS) {
-    if (cnt[a] > 0) {
-      sst[sidx[a]] = cnt[a];
-      P.seg_adapter[sidx[a]] = a;
-      atomicMax(&sh.mmax, cnt[a]);
-    }
-  }
-  __syncthreads();
-
-  // segment starts and row tiles
-  {
-    int run = 0, run_s = 0, run_l = 0;
-    for (int base = 0; base < S; base += THREADS) {
-      const int s = base + tid;
-      const int len = s < S ? sst[s] : 0;
-      const int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
-      const int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
-      int tot, tot_s, tot_l;
-      const int st = block_exclusive_scan<THREADS>(len, sh.wave_sums, &tot) + run;
-      const int os = block_exclusive_scan<THREADS>(ns, sh.wave_sums, &tot_s) + run_s;
-      const int ol = block_exclusive_scan<THREADS>(nl, sh.wave_sums, &tot_l) + run_l;
-      if (s < S) {
-        P.seg_start[s] = st;
-        for (int t = 0; t < ns; ++t) {
-          P.tiles_small[2 * (os + t)] = st + t * LORA_TILE_SMALL;
-          P.tiles_small[2 * (os + t) + 1] = s;
-        }
-        for (int t = 0; t < nl; ++t) {
-          P.tiles_large[2 * (ol + t)] = st + t * LORA_TILE_LARGE;
-          P.tiles_large[2 * (ol + t) + 1] = s;
-        }
-        sst[s] = st;
-      }
-      run += tot;
-      run_s += tot_s;
-      run_l += tot_l;
-    }
-    if (tid == 0) {
-      P.seg_start[S] = run;
-      sh.nact = run;
-      P.sum[kNTilesSmall] = run_s;
-      P.sum[kNTilesLarge] = run_l;
-    }
-  }
-  __syncthreads();
-
-  // placement cursor per adapter = start of its segment
-  for (int a = tid; a < N; a += THREADS)
-    if (cnt[a] > 0) cnt[a] = sst[sidx[a]];
-  __syncthreads();
 
   // 3. stable scatter, chunk by chunk
   const int n_active = sh.nact;

@@ -3,8 +3,11 @@
 // directions beyond the adapter's retained rank exit before reading operands).
 //
 // bf16 pools: one work item is (row tile of <= 16 rows of one segment, block
-// of 16 rank directions), computed as a 16 x 16 tile of MFMA
-// v_mfma_f32_16x16x32_bf16 products.  Operand fragments come straight from
+// of db = 16, 8 or 4 rank directions), computed as a 16 x 16 tile of MFMA
+// v_mfma_f32_16x16x32_bf16 products (directions past the block repeat its
+// last one and are not stored).  Small batches use narrow blocks, so that
+// enough workgroups share the A rows to keep the chip's CUs streaming; the
+// k order of every output, hence v, does not depend on db.  Operand fragments come straight from
 // global memory: lane l reads 16 contiguous bytes of token row (l mod 16)
 // and 16 contiguous bytes of direction row (l mod 16), at k offset
 // 8 * (l / 16) inside each 32-wide k chunk, so both operands stream in
@@ -32,11 +35,11 @@ struct ShrinkArgs {
   int32_t* seg;
   float* v;
   int ld_x, r_cap, d_in, T, ld_v;
-  int mode, nrb, rtiles, n_items;  // n_items: host item count (EXACT/BUCKETED/FULL)
+  int mode, db, nrb, rtiles, n_items;  // n_items: host item count (EXACT/BUCKETED/FULL)
 };
 
-constexpr int kDB = 16;           // rank directions per work item
 constexpr int kUnroll = 8;        // k chunks in flight per wave
+constexpr int kMinItems = 256;    // narrow the rank blocks until about this many items exist
 
 // One k chunk of the 16 x 16 tile: bf16 takes one 16x16x32 MFMA; fp32 takes
 // four 16x16x4 MFMAs, MFMA e using element e of every lane's 4 values, so
@@ -76,12 +79,13 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, a.rtiles, w)) continue;
     const int adapter = P.seg_adapter[w.seg];
     const int r = a.slot_rank[adapter];
-    const int j0 = rb * kDB;
+    const int j0 = rb * a.db;
     if (j0 >= r) continue;                      // directions beyond the retained rank
-    // rows past the tile and directions past the rank read a valid row; their
-    // results are never stored
+    const int jn = min(a.db, r - j0);           // directions of this item
+    // rows past the tile and directions past the block read a valid row (the
+    // same addresses, merged by the cache); their results are never stored
     const TI* xr = X + (size_t)P.perm[w.p0 + min(frow, w.rows - 1)] * a.ld_x + fk * VEC;
-    const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(frow, r - j0 - 1)) * a.d_in + fk * VEC;
+    const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(frow, jn - 1)) * a.d_in + fk * VEC;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = wave; c0 < nchunk; c0 += kWaves * kUnroll) {
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
       float s = 0.f;
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) s += red[q][src][e];
-      if (row < w.rows && j0 + col < r) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + col] = s;
+      if (row < w.rows && col < jn) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + col] = s;
     }
     __syncthreads();
   }
@@ -128,16 +132,21 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   a.T = T;
   a.ld_v = ld_v;
   a.mode = ls.mode;
-  a.nrb = (pool.r_cap + kDB - 1) / kDB;
   a.rtiles = host_row_tiles(ls, T, LORA_TILE_SMALL);
+  // row tiles: exact for EXACT / BUCKETED / FULL_BATCH; for PERSISTENT the
+  // bound sum_a ceil(m_a / 16) <= T / 16 + min(T, n_slots)
+  const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT
+                         ? (long)T / LORA_TILE_SMALL + std::min(T, pool.n_slots)
+                         : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
+  a.db = 16;
+  while (a.db > 4 && tiles * ((pool.r_cap + a.db - 1) / a.db) < kMinItems) a.db >>= 1;
+  a.nrb = (pool.r_cap + a.db - 1) / a.db;
   int grid;
   if (ls.mode == LORA_LAUNCH_PERSISTENT) {
     a.n_items = 0;
-    // upper bound of the device tile count: sum_a ceil(m_a / 16) <= T / 16 + min(T, n_slots)
-    const long bound = ((long)T / LORA_TILE_SMALL + std::min(T, pool.n_slots)) * a.nrb;
-    grid = (int)std::min<long>(bound, 1024);
+    grid = (int)std::min<long>(tiles * a.nrb, 1024);
   } else {
-    a.n_items = host_tile_items(ls, T, LORA_TILE_SMALL) * a.nrb;
+    a.n_items = (int)(tiles * a.nrb);
     grid = a.n_items;
   }
   if (grid <= 0 || T == 0) return hipSuccess;
