@@ -634,7 +634,7 @@ hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
     return launch_cfg<64, 64, MODE, 4, 2, 2>(a, pl, st);
   } else {
     if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4, 4, 2>(a, pl, st);
-    return launch_cfg<64, 64, MODE, 4, 2, 4>(a, pl, st);
+    return launch_cfg<64, 64, MODE, 4, 4, 2>(a, pl, st);
   }
 }
 

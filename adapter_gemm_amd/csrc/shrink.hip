@@ -4,17 +4,20 @@
 //
 // bf16 pools: one work item is (row tile of <= 16 rows of one segment, block
 // of db = 16, 8 or 4 rank directions), computed as a 16 x 16 tile of MFMA
-// v_mfma_f32_16x16x32_bf16 products (directions past the block repeat its
-// last one and are not stored).  Small batches use narrow blocks, so that
-// enough workgroups share the A rows to keep the chip's CUs streaming; the
-// k order of every output, hence v, does not depend on db.  Operand fragments come straight from
-// global memory: lane l reads 16 contiguous bytes of token row (l mod 16)
-// and 16 contiguous bytes of direction row (l mod 16), at k offset
+// v_mfma_f32_16x16x32_bf16 products.  Small batches use narrow blocks, so
+// that enough workgroups share the A rows to keep the chip's CUs streaming.
+// Operand fragments come straight from global memory: lane l reads 16
+// contiguous bytes of a token row and 16 of a direction row, at k offset
 // 8 * (l / 16) inside each 32-wide k chunk, so both operands stream in
-// 128-bit loads and A_a is read once per row tile.  The 16 waves of the
-// workgroup take interleaved k chunks (so that for decode widths every load
-// of a wave is in flight at once) and their 16 x 16 partial tiles are summed
-// through LDS in a fixed order: no atomics, bitwise reproducible.
+// 128-bit loads and A_a is read once per row tile.  Row slot l mod 16 is a
+// token row / direction for a full item; an item of few rows and directions
+// folds the k range instead: with P = 4, 8 or 16 >= max(rows, directions),
+// slot s + P q reads row / direction s over the q-th of 16 / P k slices, so
+// no two lanes load the same bytes, and the slices' partial sums (the
+// diagonal P x P blocks of the product) are added in slice order.  The 16
+// waves of the workgroup take interleaved k chunks (so that for decode
+// widths every load of a wave is in flight at once) and their partial tiles
+// are summed through LDS in a fixed order: no atomics, bitwise reproducible.
 //
 // fp32 pools use the same tiling with v_mfma_f32_16x16x4f32 (four MFMAs per
 // 16-byte load, one per element).
@@ -82,34 +85,46 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     const int j0 = rb * a.db;
     if (j0 >= r) continue;                      // directions beyond the retained rank
     const int jn = min(a.db, r - j0);           // directions of this item
-    // rows past the tile and directions past the block read a valid row (the
-    // same addresses, merged by the cache); their results are never stored
-    const TI* xr = X + (size_t)P.perm[w.p0 + min(frow, w.rows - 1)] * a.ld_x + fk * VEC;
-    const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(frow, jn - 1)) * a.d_in + fk * VEC;
+    const int span = max(w.rows, jn);
+    const int Pw = span <= 4 ? 4 : (span <= 8 ? 8 : 16);   // row slots per k slice
+    const int sl = frow % Pw, ks = frow / Pw;                // this lane's slot and k slice
+    const int nchq = (nchunk * Pw + 15) / 16;                // k chunks per slice
+    // slots past the tile's rows / the block's directions repeat a valid one;
+    // their products are never stored
+    const TI* xr = X + (size_t)P.perm[w.p0 + min(sl, w.rows - 1)] * a.ld_x + fk * VEC;
+    const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(sl, jn - 1)) * a.d_in + fk * VEC;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = wave; c0 < nchunk; c0 += kWaves * kUnroll) {
+    for (int c0 = wave; c0 < nchq; c0 += kWaves * kUnroll) {
       u32x4_t xv[kUnroll], av[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int k = (c0 + kWaves * u) * KC + fk * VEC;
-        const bool in = k < a.d_in;           // d_in % 8 == 0: a lane's group is all in or all out
-        xv[u] = in ? ld128(xr + (size_t)(c0 + kWaves * u) * KC) : u32x4_t{0, 0, 0, 0};
-        av[u] = in ? ld128(ar + (size_t)(c0 + kWaves * u) * KC) : u32x4_t{0, 0, 0, 0};
+        const int c = c0 + kWaves * u;
+        const int g = ks * nchq + c;            // this lane's chunk
+        // d_in % 8 == 0: a lane's group is all in or all out
+        const bool in = c < nchq && g * KC + fk * VEC < a.d_in;
+        xv[u] = in ? ld128(xr + (size_t)g * KC) : u32x4_t{0, 0, 0, 0};
+        av[u] = in ? ld128(ar + (size_t)g * KC) : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) acc = mfma_chunk<TI>(xv[u], av[u], acc);
     }
-    // acc[e] = partial v[row = 4 * (lane / 16) + e][direction = lane % 16]
+    // acc[e] = partial product[row = 4 * (lane / 16) + e][col = lane % 16];
+    // v[s, c] is the sum over slices q of product[s + Pw q][c + Pw q]
     red[wave][lane] = acc;
     __syncthreads();
     if (threadIdx.x < 256) {
-      const int t = threadIdx.x;              // one output each, waves summed in order
+      const int t = threadIdx.x;              // one output each, slices and waves summed in order
       const int row = t >> 4, col = t & 15;
-      const int src = (row >> 2) * 16 + col, e = row & 3;
       float s = 0.f;
+      if (row < Pw && col < Pw) {
+        for (int q = 0; q < 16 / Pw; ++q) {
+          const int i = row + Pw * q, j = col + Pw * q;
+          const int src = (i >> 2) * 16 + j, e = i & 3;
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) s += red[q][src][e];
+          for (int wv = 0; wv < kWaves; ++wv) s += red[wv][src][e];
+        }
+      }
       if (row < w.rows && col < jn) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + col] = s;
     }
     __syncthreads();
@@ -133,14 +148,15 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   a.ld_v = ld_v;
   a.mode = ls.mode;
   a.rtiles = host_row_tiles(ls, T, LORA_TILE_SMALL);
-  // row tiles: exact for EXACT / BUCKETED / FULL_BATCH; for PERSISTENT the
-  // bound sum_a ceil(m_a / 16) <= T / 16 + min(T, n_slots)
-  const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT
-                         ? (long)T / LORA_TILE_SMALL + std::min(T, pool.n_slots)
-                         : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
+  // The rank-block width (and with it each item's k folding) follows from
+  // the batch shape alone, through the bound sum_a ceil(m_a / 16) <= T / 16 +
+  // min(T, n_slots) of the row tiles, so v is the same in every launch mode.
+  const long bound = (long)T / LORA_TILE_SMALL + std::min(T, pool.n_slots);
   a.db = 16;
-  while (a.db > 4 && tiles * ((pool.r_cap + a.db - 1) / a.db) < kMinItems) a.db >>= 1;
+  while (a.db > 4 && bound * ((pool.r_cap + a.db - 1) / a.db) < kMinItems) a.db >>= 1;
   a.nrb = (pool.r_cap + a.db - 1) / a.db;
+  // row tiles: the bound for PERSISTENT, else the mode's host count
+  const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT ? bound : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
   int grid;
   if (ls.mode == LORA_LAUNCH_PERSISTENT) {
     a.n_items = 0;
