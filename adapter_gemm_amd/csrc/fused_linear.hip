@@ -351,8 +351,10 @@ __global__ __launch_bounds__(kThreads) void fused_gemm_kernel(FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path (fp32 base, pool, x and y): LDS-tiled FMA GEMM, 64 x 64 tiles,
-// each thread 4 x 4 outputs; the adapter term is a per-element rank-r dot.
+// fp32 path (fp32 base, pool, x and y): LDS-tiled FMA GEMM, 32 x 32 tiles
+// (small fp32 problems: many workgroups), 64-wide k blocks whose loads for
+// the next block are in flight while the current one is multiplied; each
+// thread 2 x 2 outputs; the adapter term is a per-element rank-r dot.
 // ---------------------------------------------------------------------------
 struct F32Args {
   const float* x;
@@ -366,10 +368,12 @@ struct F32Args {
   int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out, tiles_n;
 };
 
+constexpr int kF32Tile = 32;
+
 __global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
-  constexpr int BM = 64, BN = 64, BK = 16;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Ws[BK][BN + 4];
+  constexpr int BM = kF32Tile, BN = kF32Tile, BK = 64;
+  __shared__ float As[BK][BM + 1];
+  __shared__ float Ws[BK][BN + 1];
   const int tid = threadIdx.x;
   const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -380,41 +384,55 @@ __global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
     has_seg = seg_valid(P, a.T);
   }
 
-  const int lr = tid >> 2, lc = (tid & 3) * 4;    // staging: row, k offset
+  // staging: row lr of the tile, 8 consecutive k (d_in, ld_x, ld_w are
+  // multiples of 8 and the rows 16-byte aligned: two float4 loads, all in or
+  // all out of range)
+  const int lr = tid >> 3, lk = (tid & 7) * 8;
   const int apos = m0 + lr;
   const float* xrow = nullptr;
   if (apos < a.T) xrow = a.x + (size_t)(has_seg ? P.perm[apos] : apos) * a.ld_x;
   const float* wrow = (n0 + lr < a.d_out) ? a.W + (size_t)(n0 + lr) * a.ld_w : nullptr;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t xa[2], wa[2];
+  auto load = [&](int k0) {
+    const int k = k0 + lk;
+    const bool in = k < a.d_in;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      xa[h] = (xrow && in) ? *reinterpret_cast<const f32x4_t*>(xrow + k + 4 * h) : zero;
+      wa[h] = (wrow && in) ? *reinterpret_cast<const f32x4_t*>(wrow + k + 4 * h) : zero;
+    }
+  };
 
   const int ty = tid >> 4, tx = tid & 15;
-  float acc[4][4] = {};
+  float acc[2][2] = {};
+  load(0);
   for (int k0 = 0; k0 < a.d_in; k0 += BK) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = k0 + lc + e;
-      As[lc + e][lr] = (xrow && k < a.d_in) ? xrow[k] : 0.f;
-      Ws[lc + e][lr] = (wrow && k < a.d_in) ? wrow[k] : 0.f;
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        As[lk + 4 * h + e][lr] = xa[h][e];
+        Ws[lk + 4 * h + e][lr] = wa[h][e];
+      }
     __syncthreads();
-#pragma unroll
+    if (k0 + BK < a.d_in) load(k0 + BK);      // the next block's loads overlap these FMAs
+#pragma unroll 16
     for (int kk = 0; kk < BK; ++kk) {
-      float av[4], wv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wv[j] = Ws[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], wv[j], acc[i][j]);
+      const float a0 = As[kk][ty * 2], a1 = As[kk][ty * 2 + 1];
+      const float w0 = Ws[kk][tx * 2], w1 = Ws[kk][tx * 2 + 1];
+      acc[0][0] = fmaf(a0, w0, acc[0][0]);
+      acc[0][1] = fmaf(a0, w1, acc[0][1]);
+      acc[1][0] = fmaf(a1, w0, acc[1][0]);
+      acc[1][1] = fmaf(a1, w1, acc[1][1]);
     }
     __syncthreads();
   }
 
   const int n_active = (has_seg && a.B) ? P.sum[kNActive] : 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = m0 + ty * 4 + i;
+  for (int i = 0; i < 2; ++i) {
+    const int pos = m0 + ty * 2 + i;
     if (pos >= a.T) continue;
     const int row = has_seg ? P.perm[pos] : pos;
     int ad = -1, r = 0;
@@ -425,8 +443,8 @@ __global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
       sc = a.slot_scale[ad];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + tx * 2 + j;
       if (n >= a.d_out) continue;
       float out = acc[i][j];
       if (ad >= 0) {
@@ -482,8 +500,8 @@ hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_
     a.T = T;
     a.d_in = d_in;
     a.d_out = d_out;
-    a.tiles_n = (d_out + 63) / 64;
-    const int grid = ((T + 63) / 64) * a.tiles_n;
+    a.tiles_n = (d_out + kF32Tile - 1) / kF32Tile;
+    const int grid = ((T + kF32Tile - 1) / kF32Tile) * a.tiles_n;
     hipLaunchKernelGGL(fused_f32_kernel, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }

@@ -294,10 +294,12 @@ def main():
         roof = {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(fused_gbs / HBM_PEAK_GBS, 4)}
     else:
+        # the fp32 path multiplies with vector FMAs (fp32 vector peak), the
+        # others on MFMA at their dtype's dense peak
         pk = MFMA_PEAK_TFLOPS[mfma_dtype]
-        roof = {"bound": "mfma", "achieved": round(fused_tfs, 1), "peak": pk, "unit": "TFLOP/s",
-                "frac": round(fused_tfs / pk, 4)}
-    roof["kernel"] = DOMINANT
+        roof = {"bound": "alu" if base == "fp32" else "mfma", "achieved": round(fused_tfs, 1), "peak": pk,
+                "unit": "TFLOP/s", "frac": round(fused_tfs / pk, 4)}
+    roof["kernel"] = "fused_f32_kernel" if base == "fp32" else DOMINANT
     roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_proj
     roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_proj
     roof["traffic"] = stored_traffic(w.name)
