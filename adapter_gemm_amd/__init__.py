@@ -27,6 +27,7 @@ SEG_HEADER = 16
 EXPORTED = [
     "lora_segment_words", "lora_build_segments", "lora_plan_segments", "lora_build_segments_dev",
     "lora_shrink", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
+    "lora_fused_linear_slices", "lora_fused_slices_workspace_bytes",
     "lora_quantize_e4m3", "lora_status_string", "lora_last_error",
 ]
 
@@ -77,6 +78,8 @@ def _load():
         "lora_expand": (I32, [P, P, I32, P, P, I32, P, I32, I32, I32, P]),
         "lora_fused_linear": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P, SZ, P]),
         "lora_fused_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+        "lora_fused_linear_slices": (I32, [I32, P, P, P, I32, P, I32, I32, P, P, P, P, P, I32, P, SZ, P]),
+        "lora_fused_slices_workspace_bytes": (SZ, [I32, I32, I32, P, I32, I32]),
         "lora_quantize_e4m3": (I32, [P, I32, I32, I32, P, I32, P, P]),
         "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lora_last_error": (ctypes.c_char_p, []),
@@ -193,6 +196,33 @@ def fused_workspace(T: int, d_in: int, d_out: int, base_dtype: int, flags: int =
     import torch
     n = fused_workspace_bytes(T, d_in, d_out, base_dtype, flags)
     return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fused_slices_workspace(T: int, d_in: int, d_outs, base_dtype: int, flags: int = 0, device="cuda"):
+    """A workspace tensor for a sliced fused call (None when none is needed)."""
+    import torch
+    n = len(d_outs)
+    arr = (ctypes.c_int32 * n)(*[int(d) for d in d_outs])
+    nb = int(_lib.lora_fused_slices_workspace_bytes(n, T, d_in, arr, base_dtype, flags))
+    return None if nb == 0 else torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def fused_linear_slices(bases, pools, seg, x, vs, ys, flags: int = 0, workspace=None, stream=None) -> None:
+    """Several projections of one x in one launch: slice s is fused_linear(bases[s],
+    pools[s], seg, x, vs[s], ys[s]); pools / vs None for the base products alone."""
+    n = len(bases)
+    T, d_in = int(x.shape[0]), int(x.shape[1])
+    b_arr = (BaseDesc * n)(*bases)
+    p_arr = None if pools is None else (PoolDesc * n)(*pools)
+    v_arr = None if vs is None else (ctypes.c_void_p * n)(*[v.data_ptr() for v in vs])
+    ldv = None if vs is None else (ctypes.c_int32 * n)(*[_ld(v) for v in vs])
+    y_arr = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    ldy = (ctypes.c_int32 * n)(*[_ld(y) for y in ys])
+    d_out = (ctypes.c_int32 * n)(*[int(y.shape[1]) for y in ys])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lora_fused_linear_slices(n, b_arr, p_arr, _ptr(seg), T, x.data_ptr(), _ld(x), d_in, d_out,
+                                         v_arr, ldv, y_arr, ldy, flags, _ptr(workspace), ws_bytes,
+                                         _stream(stream)), "lora_fused_linear_slices")
 
 
 def fused_linear(base: BaseDesc, pool: Optional[PoolDesc], seg, x, v, y, flags: int = 0, workspace=None,

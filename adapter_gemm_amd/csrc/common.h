@@ -117,6 +117,26 @@ struct FusedPlan {
 
 // r_cap: the adapter pool's rank capacity, 0 without a pool
 FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap);
+
+// One output slice of a fused launch (slices share x, the rows and seg).
+struct FusedSlice {
+  lora_base_t base;
+  const lora_pool_t* pool;   // NULL: the base product alone
+  const float* v;
+  int ld_v;
+  void* y;
+  int ld_y;
+  int d_out;
+};
+// The plan of one launch over n slices (dma false: the slices go one by one).
+FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int base_dtype, int flags);
+hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, int n, const int32_t* seg, int T,
+                                   const void* x, int ld_x, const float* s_x, int d_in, int flags, void* part_ws,
+                                   hipStream_t st);
+hipError_t launch_fused_slices(const FusedSlice* sl, int n, int32_t* seg, int T, const void* x, int ld_x, int d_in,
+                               int flags, void* workspace, hipStream_t st);
+size_t fused_slices_workspace_bytes(int T, int d_in, const int32_t* d_out, const int32_t* r_cap, int n,
+                                    int base_dtype, int flags);
 bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, int base_dtype, int flags,
                     const lora_pool_t* pool);
 hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,

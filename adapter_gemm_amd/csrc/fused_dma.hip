@@ -26,6 +26,12 @@
 // group's rows, held as a bf16 tile in LDS with rows of other groups masked
 // to zero.  The products land on the same accumulators as the base GEMM.
 //
+// Output slices.  One launch can cover several projections of the same x
+// (q / k / v, gate / up: "LoRAForge" 4, S slices per layer), each with its
+// own W0 rows, adapter pool, v and y: the tile grid's columns are the slices'
+// column tiles laid end to end, and a workgroup takes the slice of its column
+// tile (slices start at tile boundaries; a slice's last tile may be ragged).
+//
 // Split K.  When the output has too few tiles to fill the chip (decode
 // batches), the k range is split over `splits` workgroups per tile and one
 // more workgroup per tile runs the adapter phase alone.  Each writes its
@@ -46,6 +52,22 @@ constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer, gfx9-family descr
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+constexpr int kMaxSlices = 4;
+
+// One output slice of a launch (everything that differs between slices).
+struct SliceArgs {
+  const void* W;
+  const float* w_scale;
+  const void* B;
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  const float* v;
+  void* y;
+  uint32_t w_bytes, b_bytes, v_bytes;
+  int ld_w, d_out, r_cap, ld_v, ld_y;
+  int tn0;                // first column tile of the slice
+};
+
 struct DmaArgs {
   const void* x;
   const void* W;
@@ -62,6 +84,8 @@ struct DmaArgs {
   uint32_t x_bytes, w_bytes, v_bytes, b_bytes;   // descriptor ranges (b: the whole B pool)
   int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out;
   int tiles_m, tiles_n, group_m, nk, splits, lora_split;
+  int n_slices;           // > 1: the per-slice fields above come from sl[]
+  SliceArgs sl[kMaxSlices];
 };
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
@@ -206,7 +230,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     tm = first_m + in % gm;
     tn = in / gm;
   }
-  const int m0 = tm * BM, n0 = tn * BN;
+  int n0 = tn * BN;
+  if (a.n_slices > 1) {
+    // constant indices keep the slice fields in scalar registers
+    SliceArgs q = a.sl[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSlices; ++s)
+      if (s < a.n_slices && tn >= a.sl[s].tn0) q = a.sl[s];
+    a.W = q.W;
+    a.w_scale = q.w_scale;
+    a.B = q.B;
+    a.slot_rank = q.slot_rank;
+    a.slot_scale = q.slot_scale;
+    a.v = q.v;
+    a.y = q.y;
+    a.w_bytes = q.w_bytes;
+    a.b_bytes = q.b_bytes;
+    a.v_bytes = q.v_bytes;
+    a.ld_w = q.ld_w;
+    a.d_out = q.d_out;
+    a.r_cap = q.r_cap;
+    a.ld_v = q.ld_v;
+    a.ld_y = q.ld_y;
+    n0 = (tn - q.tn0) * BN;
+  }
+  const int m0 = tm * BM;
 
   SegPtrs P;
   bool has_seg = a.seg != nullptr;
@@ -717,45 +765,101 @@ bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, i
   return true;
 }
 
-hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,
-                            const int32_t* seg, int T, const void* x, int ld_x, const float* s_x, const float* v,
-                            int ld_v, void* y, int ld_y, int d_in, int d_out, int flags, void* part_ws,
-                            hipStream_t st) {
-  DmaArgs a;
+FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int base_dtype, int flags) {
+  int total = 0, r_cap = 0;
+  for (int s = 0; s < n; ++s) {
+    total += sl[s].d_out;
+    if (sl[s].pool) r_cap = std::max(r_cap, sl[s].pool->r_cap);
+  }
+  FusedPlan pl = plan_fused(T, d_in, total, base_dtype, flags, r_cap);
+  if (n > 1 && pl.dma) {
+    // column tiles per slice; one launch only without a k split
+    int tn = 0;
+    for (int s = 0; s < n; ++s) tn += (sl[s].d_out + pl.bn - 1) / pl.bn;
+    pl.tiles_n = tn;
+    pl.tiles = pl.tiles_m * tn;
+    if (pl.splits > 1 || n > kMaxSlices) pl.dma = false;
+  }
+  return pl;
+}
+
+hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, int n, const int32_t* seg, int T,
+                                   const void* x, int ld_x, const float* s_x, int d_in, int flags, void* part_ws,
+                                   hipStream_t st) {
+  const lora_base_t& base = sl[0].base;
   const bool w8a8 = base.dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
+  const int wel = base.dtype == LORA_BF16 ? 2 : 1;
+  auto fill = [&](SliceArgs& q, const FusedSlice& f) {
+    q.W = f.base.W;
+    q.w_scale = f.base.w_scale;
+    q.B = f.pool ? f.pool->B : nullptr;
+    q.slot_rank = f.pool ? f.pool->slot_rank : nullptr;
+    q.slot_scale = f.pool ? f.pool->slot_scale : nullptr;
+    q.v = f.v;
+    q.y = f.y;
+    q.w_bytes = (uint32_t)((long)f.d_out * f.base.ld_w * wel);
+    q.b_bytes = f.pool ? (uint32_t)((long)f.pool->n_slots * f.pool->d_out * f.pool->r_cap * 2) : 0;
+    q.v_bytes = f.pool ? (uint32_t)((long)T * f.ld_v * 4) : 0;
+    q.ld_w = f.base.ld_w;
+    q.d_out = f.d_out;
+    q.r_cap = f.pool ? f.pool->r_cap : 0;
+    q.ld_v = f.ld_v;
+    q.ld_y = f.ld_y;
+    q.tn0 = 0;
+  };
+  DmaArgs a;
+  SliceArgs q0;
+  fill(q0, sl[0]);
   a.x = x;
-  a.W = base.W;
-  a.w_scale = base.w_scale;
+  a.W = q0.W;
+  a.w_scale = q0.w_scale;
   a.s_x = s_x;
-  a.B = pool ? pool->B : nullptr;
-  a.slot_rank = pool ? pool->slot_rank : nullptr;
-  a.slot_scale = pool ? pool->slot_scale : nullptr;
+  a.B = q0.B;
+  a.slot_rank = q0.slot_rank;
+  a.slot_scale = q0.slot_scale;
   a.seg = seg;
-  a.v = v;
-  a.y = y;
+  a.v = q0.v;
+  a.y = q0.y;
   a.part = static_cast<float*>(part_ws);
   a.counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(part_ws) + pl.part_bytes);
   a.x_bytes = (uint32_t)((long)T * ld_x * (w8a8 ? 1 : 2));
-  a.w_bytes = (uint32_t)((long)d_out * base.ld_w * (base.dtype == LORA_BF16 ? 2 : 1));
-  a.b_bytes = pool ? (uint32_t)((long)pool->n_slots * pool->d_out * pool->r_cap * 2) : 0;
-  a.v_bytes = pool ? (uint32_t)((long)T * ld_v * 4) : 0;
-  a.r_cap = pool ? pool->r_cap : 0;
-  a.ld_v = ld_v;
-  a.ld_y = ld_y;
+  a.w_bytes = q0.w_bytes;
+  a.b_bytes = q0.b_bytes;
+  a.v_bytes = q0.v_bytes;
+  a.r_cap = q0.r_cap;
+  a.ld_v = q0.ld_v;
+  a.ld_y = q0.ld_y;
   a.ld_x = ld_x;
-  a.ld_w = base.ld_w;
+  a.ld_w = q0.ld_w;
   a.T = T;
   a.d_in = d_in;
-  a.d_out = d_out;
+  a.d_out = q0.d_out;
   a.tiles_m = pl.tiles_m;
   a.tiles_n = pl.tiles_n;
   a.group_m = std::min(pl.tiles_m, 8);
   a.nk = pl.nk;
   a.splits = pl.splits;
-  a.lora_split = pool ? pl.lora_split : 0;
+  a.lora_split = sl[0].pool ? pl.lora_split : 0;
+  a.n_slices = n > 1 ? n : 1;
+  if (n > 1) {
+    int tn0 = 0;
+    for (int s = 0; s < n; ++s) {
+      fill(a.sl[s], sl[s]);
+      a.sl[s].tn0 = tn0;
+      tn0 += (sl[s].d_out + pl.bn - 1) / pl.bn;
+    }
+  }
   if (base.dtype == LORA_BF16) return launch_mode<kBF16>(a, pl, st);
   if (w8a8) return launch_mode<kW8A8>(a, pl, st);
   return launch_mode<kW8A16>(a, pl, st);
+}
+
+hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,
+                            const int32_t* seg, int T, const void* x, int ld_x, const float* s_x, const float* v,
+                            int ld_v, void* y, int ld_y, int d_in, int d_out, int flags, void* part_ws,
+                            hipStream_t st) {
+  const FusedSlice one{base, pool, v, ld_v, y, ld_y, d_out};
+  return launch_fused_dma_slices(pl, &one, 1, seg, T, x, ld_x, s_x, d_in, flags, part_ws, st);
 }
 
 }  // namespace lora

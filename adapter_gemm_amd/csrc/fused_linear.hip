@@ -25,6 +25,8 @@
 //    streams.
 #include "common.h"
 
+#include <algorithm>
+
 namespace lora {
 namespace {
 
@@ -549,6 +551,54 @@ hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_
   if (base.dtype == LORA_BF16) return launch_mode<kBF16>(a, st);
   if (!w8a8) return launch_mode<kW8A16>(a, st);
   return launch_mode<kW8A8>(a, st);
+}
+
+size_t fused_slices_workspace_bytes(int T, int d_in, const int32_t* d_out, const int32_t* r_cap, int n,
+                                    int base_dtype, int flags) {
+  // a merged launch needs the W8A8 codes only; slices launched one by one
+  // use their own plans' workspaces, one after another
+  size_t need = fused_quant_bytes(T, d_in, flags, base_dtype);
+  for (int s = 0; s < n; ++s)
+    need = std::max(need, fused_workspace_bytes(T, d_in, d_out[s], base_dtype, flags, r_cap[s]));
+  return need;
+}
+
+hipError_t launch_fused_slices(const FusedSlice* sl, int n, int32_t* seg, int T, const void* x, int ld_x, int d_in,
+                               int flags, void* workspace, hipStream_t st) {
+  if (T == 0 || n <= 0) return hipSuccess;
+  const int bt = sl[0].base.dtype;
+  const bool w8a8 = bt == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
+  const int ld_q = (d_in + 15) / 16 * 16;
+  FusedPlan pl{};
+  bool merged = n > 1 && bt != LORA_F32;
+  if (merged) {
+    pl = plan_fused_slices(T, d_in, sl, n, bt, flags);
+    merged = pl.dma;
+    for (int s = 0; merged && s < n; ++s)
+      merged = fused_dma_fits(pl, T, w8a8 ? ld_q : ld_x, sl[s].d_out, sl[s].base.ld_w, bt, flags, sl[s].pool);
+  }
+  if (!merged) {
+    for (int s = 0; s < n; ++s) {
+      if (sl[s].d_out == 0) continue;
+      hipError_t e = launch_fused(sl[s].base, sl[s].pool, seg, T, x, ld_x, sl[s].v, sl[s].ld_v, sl[s].y, sl[s].ld_y,
+                                  d_in, sl[s].d_out, flags, workspace, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const void* xin = x;
+  int ld_in = ld_x;
+  float* s_x = nullptr;
+  if (w8a8) {
+    uint8_t* q = static_cast<uint8_t*>(workspace);
+    s_x = reinterpret_cast<float*>(q + (size_t)T * ld_q);
+    hipError_t e = launch_quantize_e4m3(x, T, d_in, ld_x, q, ld_q, s_x, st);
+    if (e != hipSuccess) return e;
+    xin = q;
+    ld_in = ld_q;
+  }
+  return launch_fused_dma_slices(pl, sl, n, seg, T, xin, ld_in, s_x, d_in, flags,
+                                 static_cast<uint8_t*>(workspace) + fused_quant_bytes(T, d_in, flags, bt), st);
 }
 
 }  // namespace lora

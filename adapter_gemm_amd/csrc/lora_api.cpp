@@ -216,10 +216,13 @@ size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_
   return lora::fused_workspace_bytes(T, d_in, d_out, base_dtype, flags, 8);
 }
 
-int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
-                      const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,
-                      int32_t d_in, int32_t d_out, int32_t flags, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+// Arguments of one fused product (everything but the workspace).
+int check_fused(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T, const void* x,
+                int32_t ld_x, const float* v, int32_t ld_v, const void* y, int32_t ld_y, int32_t d_in, int32_t d_out,
+                int32_t flags) {
   if (!base || !base->W) return LORA_E_ARG;
   if (T < 0 || d_in < 0 || d_out < 0 || (T > 0 && (!x || !y))) return LORA_E_ARG;
   if (flags & ~LORA_FLAG_ACT_QUANT_E4M3) return LORA_E_ARG;
@@ -245,6 +248,19 @@ int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const in
   if (bt != LORA_FP8_E4M3 && base->ld_w % 8) return LORA_E_ALIGN;
   if (!aligned16(x) || !aligned16(y) || !aligned16(base->W)) return LORA_E_ALIGN;
   if (x == y) return LORA_E_ARG;
+  return LORA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
+                      const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,
+                      int32_t d_in, int32_t d_out, int32_t flags, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  const int st = check_fused(base, pool, seg, T, x, ld_x, v, ld_v, y, ld_y, d_in, d_out, flags);
+  if (st != LORA_OK) return st;
+  const int bt = base->dtype;
   const size_t need = lora::fused_workspace_bytes(T, d_in, d_out, bt, flags, pool ? pool->r_cap : 0);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return LORA_E_SIZE;
@@ -253,6 +269,48 @@ int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const in
   if (T == 0 || d_out == 0) return LORA_OK;
   return hip_status(lora::launch_fused(*base, pool, const_cast<int32_t*>(seg), T, x, ld_x, v, ld_v, y, ld_y, d_in,
                                        d_out, flags, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_fused_slices_workspace_bytes(int32_t n_slices, int32_t T, int32_t d_in, const int32_t* d_out,
+                                         int32_t base_dtype, int32_t flags) {
+  if (n_slices <= 0 || !d_out || T <= 0 || d_in <= 0) return 0;
+  if (base_dtype != LORA_F32 && base_dtype != LORA_BF16 && base_dtype != LORA_FP8_E4M3) return 0;
+  std::vector<int32_t> rc(n_slices, 8);   // as lora_fused_workspace_bytes: the smallest rank capacity
+  for (int s = 0; s < n_slices; ++s)
+    if (d_out[s] < 0) return 0;
+  return lora::fused_slices_workspace_bytes(T, d_in, d_out, rc.data(), n_slices, base_dtype, flags);
+}
+
+int lora_fused_linear_slices(int32_t n_slices, const lora_base_t* bases, const lora_pool_t* pools,
+                             const int32_t* seg, int32_t T, const void* x, int32_t ld_x, int32_t d_in,
+                             const int32_t* d_out, const float* const* v, const int32_t* ld_v, void* const* y,
+                             const int32_t* ld_y, int32_t flags, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (n_slices < 1 || !bases || !d_out || !y || !ld_y || ((pools != nullptr) != (v != nullptr))) return LORA_E_ARG;
+  if (pools && !ld_v) return LORA_E_ARG;
+  std::vector<lora::FusedSlice> sl(n_slices);
+  std::vector<int32_t> rc(n_slices, 0);
+  for (int s = 0; s < n_slices; ++s) {
+    const lora_pool_t* pool = pools ? &pools[s] : nullptr;
+    const float* vs = v ? v[s] : nullptr;
+    const int32_t lv = v ? ld_v[s] : 0;
+    const int st = check_fused(&bases[s], pool, seg, T, x, ld_x, vs, lv, y[s], ld_y[s], d_in, d_out[s], flags);
+    if (st != LORA_OK) return st;
+    if (bases[s].dtype != bases[0].dtype) return LORA_E_DTYPE;
+    for (int o = 0; o < s; ++o)
+      if (y[o] == y[s]) return LORA_E_ARG;            // each slice writes its own output
+    sl[s] = lora::FusedSlice{bases[s], pool, vs, lv, y[s], ld_y[s], d_out[s]};
+    rc[s] = pool ? pool->r_cap : 0;
+  }
+  const int bt = bases[0].dtype;
+  const size_t need = lora::fused_slices_workspace_bytes(T, d_in, d_out, rc.data(), n_slices, bt, flags);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return LORA_E_SIZE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LORA_E_ALIGN;
+  }
+  if (T == 0) return LORA_OK;
+  return hip_status(lora::launch_fused_slices(sl.data(), n_slices, const_cast<int32_t*>(seg), T, x, ld_x, d_in,
+                                              flags, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int lora_quantize_e4m3(const void* x, int32_t T, int32_t d, int32_t ld_x, uint8_t* q, int32_t ld_q, float* s_x,

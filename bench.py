@@ -28,6 +28,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
+# projections that read the same input and share one fused launch
+# (a decoder layer's q / k / v and gate / up)
+SLICE_GROUPS = {"llama_layer": [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"],
+                                ["down_proj"]]}
 CACHE_BYTES = 256 << 20
 METRIC = "multi-LoRA linear tokens/s; achieved HBM GB/s (decode) & MFMA % (prefill)"
 
@@ -39,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_bgmv")
     ap.add_argument("--w8a8", action="store_true", help="fp8 base: quantise activations per token")
+    ap.add_argument("--no-slices", action="store_true",
+                    help="one fused call per projection (default: projections of one input share a call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -183,6 +189,11 @@ def main():
     n_rot = max(1, -(-2 * CACHE_BYTES // max(inst_bytes, 1)))
     n_rot = min(n_rot, 64)
     flags = agm.FLAG_ACT_QUANT_E4M3 if args.w8a8 else 0
+    names = [p.name for p in w.projections]
+    if w.name in SLICE_GROUPS and not args.no_slices:
+        groups = [[names.index(n) for n in g] for g in SLICE_GROUPS[w.name]]
+    else:
+        groups = [[j] for j in range(len(names))]
     insts = []
     for r in range(n_rot):
         inst = []
@@ -195,31 +206,49 @@ def main():
             bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p.base_dtype]
             c["wsp"] = agm.fused_workspace(T, p.d_in, p.d_out, bt, flags, device=dev)
             inst.append(c)
+        gws = []
+        for g in groups:
+            p0 = inst[g[0]]["p"]
+            bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p0.base_dtype]
+            gws.append(agm.fused_slices_workspace(T, p0.d_in, [inst[j]["p"].d_out for j in g], bt, flags, device=dev)
+                       if len(g) > 1 else None)
         seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=dev)
-        insts.append((inst, seg, ids.clone(), act.clone()))
+        insts.append((inst, seg, ids.clone(), act.clone(), gws))
     torch.cuda.synchronize()
     print(f"# {n_rot} rotated instance(s) of {inst_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     n_proj = len(projs)
 
+    n_groups = len(groups)
+
     def step(i, ev=None):
-        inst, seg, ids_d, act_d = insts[i % n_rot]
+        inst, seg, ids_d, act_d, gws = insts[i % n_rot]
         if ev is not None:
             ev["seg"][0].record(stream)
         agm.build_segments_dev(ids_d, act_d, n_slots, seg)
         if ev is not None:
             ev["seg"][1].record(stream)
-        for j, c in enumerate(inst):
+        for gi, g in enumerate(groups):
+            x = inst[g[0]]["x"]                      # the group's one input
+            for j in g:
+                c = inst[j]
+                if ev is not None:
+                    ev["shrink"][2 * j].record(stream)
+                agm.shrink(c["pool"], seg, T, None, x, c["v"], launch=agm.LAUNCH_PERSISTENT)
+                if ev is not None:
+                    ev["shrink"][2 * j + 1].record(stream)
             if ev is not None:
-                ev["shrink"][2 * j].record(stream)
-            agm.shrink(c["pool"], seg, T, None, c["x"], c["v"], launch=agm.LAUNCH_PERSISTENT)
+                ev["fused"][2 * gi].record(stream)
+            if len(g) == 1:
+                c = inst[g[0]]
+                agm.fused_linear(c["base"], c["pool"], seg, x, c["v"], c["y"], flags=flags, workspace=c["wsp"])
+            else:
+                agm.fused_linear_slices([inst[j]["base"] for j in g], [inst[j]["pool"] for j in g], seg, x,
+                                        [inst[j]["v"] for j in g], [inst[j]["y"] for j in g], flags=flags,
+                                        workspace=gws[gi])
             if ev is not None:
-                ev["shrink"][2 * j + 1].record(stream)
-                ev["fused"][2 * j].record(stream)
-            agm.fused_linear(c["base"], c["pool"], seg, c["x"], c["v"], c["y"], flags=flags, workspace=c["wsp"])
-            if ev is not None:
-                ev["fused"][2 * j + 1].record(stream)
+                ev["fused"][2 * gi + 1].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -242,7 +271,7 @@ def main():
     # above comes from the run without them.
     def mk(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    evs = [{"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_proj)} for _ in range(args.steps)]
+    evs = [{"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_groups)} for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
@@ -252,7 +281,8 @@ def main():
         per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
         for j in range(n_proj):
             per["shrink"] += ev["shrink"][2 * j].elapsed_time(ev["shrink"][2 * j + 1])
-            per["fused"] += ev["fused"][2 * j].elapsed_time(ev["fused"][2 * j + 1])
+        for gi in range(n_groups):
+            per["fused"] += ev["fused"][2 * gi].elapsed_time(ev["fused"][2 * gi + 1])
     per = {k: v / args.steps for k, v in per.items()}   # ms per step
 
     if args.calibrate_copy_mb:
@@ -266,7 +296,8 @@ def main():
     live = w.live()
     n_act = int(live.sum())
     alg = {"fused_bytes": 0, "fused_flops": 0, "shrink_bytes": 0, "shrink_flops": 0}
-    for pr in projs:
+    first_of_group = {g[0] for g in groups}
+    for jp, pr in enumerate(projs):
         p = pr["p"]
         el = 2 if p.data_dtype == "bf16" else 4
         wel = 1 if p.base_dtype == "fp8" else (2 if p.base_dtype == "bf16" else 4)
@@ -276,8 +307,9 @@ def main():
         adapters_A = int((ranks * p.d_in).sum()) * el
         adapters_B = int((ranks * p.d_out).sum()) * el
         v_bytes = int(rows_r.sum()) * 4
+        x_once = T * p.d_in * el if jp in first_of_group else 0    # a group reads its input once
         alg["fused_bytes"] += (p.d_out * p.d_in * wel + (4 * p.d_out if p.base_dtype == "fp8" else 0)
-                               + T * p.d_in * el + T * p.d_out * el + adapters_B + v_bytes)
+                               + x_once + T * p.d_out * el + adapters_B + v_bytes)
         alg["fused_flops"] += 2 * T * p.d_in * p.d_out + 2 * int(rows_r.sum()) * p.d_out
         alg["shrink_bytes"] += adapters_A + n_act * p.d_in * el + v_bytes
         alg["shrink_flops"] += 2 * int(rows_r.sum()) * p.d_in
@@ -300,8 +332,8 @@ def main():
         roof = {"bound": "alu" if base == "fp32" else "mfma", "achieved": round(fused_tfs, 1), "peak": pk,
                 "unit": "TFLOP/s", "frac": round(fused_tfs / pk, 4)}
     roof["kernel"] = "fused_f32_kernel" if base == "fp32" else DOMINANT
-    roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_proj
-    roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_proj
+    roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_groups
+    roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_groups
     roof["traffic"] = stored_traffic(w.name)
 
     value = T / (ms_step * 1e-3)
@@ -320,8 +352,11 @@ def main():
         "data": "synthetic (seeded generators; Llama-shaped; random-init adapters)",
         "config": {"workload": f"{w.name}: {w.description}",
                    "path": "build_segments_dev -> shrink (persistent) -> fused_linear"
+                           + (" (one sliced launch per group: " + ", ".join("/".join(names[j] for j in g)
+                                                                           for g in groups if len(g) > 1) + ")"
+                              if any(len(g) > 1 for g in groups) else "")
                            + (" W8A8" if args.w8a8 else (" W8A16" if base == "fp8" else "")),
-                   "T": T, "projections": n_proj, "live_rows": n_act,
+                   "T": T, "projections": n_proj, "fused_launches": n_groups, "live_rows": n_act,
                    "distinct_adapters": len(w.touched_slots()), "rotated_instances": n_rot},
         "roofline": roof,
         "kernels_us_per_step": {"build_segments": round(per["seg"] * 1e3, 2),

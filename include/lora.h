@@ -21,6 +21,8 @@
  *   lora_expand                  y += s_a B_a v     (unfused up-projection)
  *   lora_fused_linear            y = W0 x (+ s_a B_a v in the epilogue),
  *                                bf16 / fp32 / fp8-e4m3 base
+ *   lora_fused_linear_slices     the same for several projections of one x
+ *                                (q / k / v, gate / up) in one launch
  *   lora_quantize_e4m3           per-token fp8 activation quantisation used
  *                                by the fp8 W8A8 base product
  *
@@ -254,6 +256,38 @@ int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const in
 /* Workspace bytes lora_fused_linear needs for this call shape (with or
  * without an adapter pool; the size with a pool covers both). */
 size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags);
+
+/*
+ * Fused linear over several output slices of one input in one launch
+ * ("LoRAForge" 4: the slices of a layer's fused projections, such as q / k /
+ * v or gate / up, each with its own weights and adapters).  Slice s is
+ * exactly lora_fused_linear with bases[s], pools[s], v[s], ld_v[s], y[s],
+ * ld_y[s] and d_out[s]; x, ld_x, seg, T, d_in and flags are shared:
+ *   y_s[i, n] = epi_s( sum_k x[i, k] * W0_s[n, k] )
+ *               + [live_i] * s_a * sum_{j < r_a} v_s[p(i), j] * B_{s,a}[n, j]
+ * The slices' column tiles share one grid, so narrow slices (k / v of a
+ * grouped-query layer) still fill the GPU.
+ *   bases    n_slices base descriptors of one dtype
+ *   pools, v NULL, NULL for the base products alone; else n_slices pools over
+ *            the same slot ids (seg is shared) and their v buffers
+ *   y        n_slices distinct outputs
+ *   workspace at least lora_fused_slices_workspace_bytes(n_slices, T, d_in,
+ *            d_out, bases[0].dtype, flags) bytes, 256-byte aligned.
+ * Up to 4 slices share a launch; more, or shapes the pipelined kernel does
+ * not take, run slice by slice on the stream.  A slice's tile shape can
+ * differ from a lone call's, so results agree with lora_fused_linear's to
+ * the output's rounding, not bit for bit.  Errors: as lora_fused_linear,
+ * for any slice; LORA_E_DTYPE if the base dtypes differ.
+ */
+int lora_fused_linear_slices(int32_t n_slices, const lora_base_t* bases, const lora_pool_t* pools,
+                             const int32_t* seg, int32_t T, const void* x, int32_t ld_x, int32_t d_in,
+                             const int32_t* d_out, const float* const* v, const int32_t* ld_v, void* const* y,
+                             const int32_t* ld_y, int32_t flags, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes lora_fused_linear_slices needs for this call shape. */
+size_t lora_fused_slices_workspace_bytes(int32_t n_slices, int32_t T, int32_t d_in, const int32_t* d_out,
+                                         int32_t base_dtype, int32_t flags);
 
 /*
  * Per-token activation quantisation for the W8A8 base product ("EpiLoRA" 2

@@ -205,3 +205,34 @@ def test_quant_and_dev_builder_validation():
     # a small output (10 tiles of 64 x 64): 2 k splits + 1 adapter split per tile
     assert lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0) == 10 * 3 * 64 * 64 * 4 + 10 * 4
     assert lib.lora_fused_workspace_bytes(0, 64, 64, agm.BF16, 0) == 0
+
+
+def test_fused_slices_host_checks():
+    """Sizes and argument errors of the sliced fused call (no device work:
+    every check runs before anything is enqueued)."""
+    lib = agm.lib()
+    d = (ctypes.c_int32 * 2)(264, 136)
+    assert lib.lora_fused_slices_workspace_bytes(0, 100, 1024, d, agm.BF16, 0) == 0
+    # slices whose merged plan would split k run one by one: the larger lone need
+    lone = max(lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0),
+               lib.lora_fused_workspace_bytes(100, 1024, 136, agm.BF16, 0))
+    assert lib.lora_fused_slices_workspace_bytes(2, 100, 1024, d, agm.BF16, 0) == lone > 0
+    # a merged launch needs no partial tiles
+    big = (ctypes.c_int32 * 3)(4096, 1024, 1024)
+    assert lib.lora_fused_slices_workspace_bytes(3, 2048, 4096, big, agm.BF16, 0) == 0
+    # errors: no slices; base dtypes that differ
+    E_ARG, E_DTYPE = 1, 4
+    assert lib.lora_fused_linear_slices(0, None, None, None, 0, None, 0, 0, None, None, None, None, None, 0,
+                                        None, 0, None) == E_ARG
+    fake = 1 << 20                                   # aligned, never dereferenced
+    bases = (agm.BaseDesc * 2)(agm.BaseDesc(fake, None, agm.BF16, 64), agm.BaseDesc(fake, None, agm.F32, 64))
+    ys = (ctypes.c_void_p * 2)(2 * fake, 3 * fake)
+    ldy = (ctypes.c_int32 * 2)(8, 8)
+    dd = (ctypes.c_int32 * 2)(8, 8)
+    assert lib.lora_fused_linear_slices(2, bases, None, None, 8, fake, 64, 64, dd, None, None, ys, ldy, 0,
+                                        None, 0, None) == E_DTYPE
+    # two slices writing one output
+    same = (agm.BaseDesc * 2)(agm.BaseDesc(fake, None, agm.BF16, 64), agm.BaseDesc(fake, None, agm.BF16, 64))
+    ys2 = (ctypes.c_void_p * 2)(2 * fake, 2 * fake)
+    assert lib.lora_fused_linear_slices(2, same, None, None, 8, fake, 64, 64, dd, None, None, ys2, ldy, 0,
+                                        None, 0, None) == E_ARG

@@ -262,6 +262,82 @@ def test_fused_pipelined_parity(case):
             assert rel_l2(y8, ref8) <= TOL["bf16"] and row_rel_l2(y8, ref8) <= TOL["bf16"]
 
 
+# ---- several output slices of one x in one launch (q / k / v, gate / up) -------
+
+# merged launches on 64- and 256-row tiles with ragged slice ends, a shape
+# whose merged plan would split k (the slices then run one by one), and fp8
+SLICES = {
+    "qkv_64tile": ("llama_layer", dict(n_slots=96, n_req=3, prefill_len=40, n_decode=70,
+                                       shapes=[("q", 1024, 1024), ("k", 1024, 264), ("v", 1024, 264)])),
+    "qkv_split_fallback": ("llama_layer", dict(n_slots=40, n_req=2, prefill_len=20, n_decode=60,
+                                               shapes=[("q", 512, 264), ("k", 512, 136), ("v", 512, 136)])),
+    "gate_up_256": ("llama_layer", dict(n_slots=96, n_req=7, prefill_len=300, n_decode=4,
+                                        shapes=[("gate", 512, 2056), ("up", 512, 2056)])),
+    "fp8_two": ("fp8_fused", [904, 520]),
+}
+
+
+def _slice_setup(case):
+    name, kw = SLICES[case]
+    if name == "fp8_fused":
+        ws = [make_workload(name, T=200, d_in=1024, d_out=d, n_slots=32, r=64) for d in kw]
+        assert all(np.array_equal(ws[0].ids, x.ids) for x in ws)
+        return ws[0], [DevProjection(x, x.projections[0]) for x in ws], ws
+    w = make_workload(name, **kw)
+    return w, [DevProjection(w, p) for p in w.projections], [w] * len(w.projections)
+
+
+@pytest.mark.parametrize("case", list(SLICES))
+def test_fused_slices_parity(case):
+    w, dps, ws = _slice_setup(case)
+    p0 = dps[0].p
+    seg, s = segments(w, p0.n_slots)
+    x, x_host = dps[0].x, dps[0].x_host          # one input for every slice
+    bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p0.base_dtype]
+    vs = []
+    for dp in dps:
+        v = torch.zeros(w.T, dp.p.r_cap, device=DEV)
+        agm.shrink(dp.pool, seg, w.T, s, x, v)
+        vs.append(v)
+    d_outs = [dp.p.d_out for dp in dps]
+    flag_sets = [0, agm.FLAG_ACT_QUANT_E4M3] if p0.base_dtype == "fp8" else [0]
+    for flags in flag_sets:
+        wsp = agm.fused_slices_workspace(w.T, p0.d_in, d_outs, bt, flags, device=DEV)
+        ys = [torch.full((w.T, dp.p.d_out), float("nan"), device=DEV).to(dp.ydtype) for dp in dps]
+        agm.fused_linear_slices([dp.base for dp in dps], [dp.pool for dp in dps], seg, x, vs, ys, flags=flags,
+                                workspace=wsp)
+        torch.cuda.synchronize()
+        for dp, wk, y in zip(dps, ws, ys):
+            got = to_f64(y)
+            args = dp.oracle_args(wk)[1:]
+            if flags:
+                ref = oracle.linear_w8a8(x_host, dp.w0_host[0], dp.w0_host[1], *args)
+                tol = TOL["bf16"]
+            else:
+                ref = oracle.linear(x_host, dp.w0_host, *args)
+                tol = _tol(dp.p)
+            assert np.isfinite(got).all(), (case, dp.p.name)
+            assert rel_l2(got, ref) <= tol, (case, dp.p.name, flags, rel_l2(got, ref))
+            assert row_rel_l2(got, ref) <= tol, (case, dp.p.name, flags)
+            # the same product as a lone call on this slice, to the output's rounding
+            y1 = torch.full_like(y, float("nan"))
+            ws1 = agm.fused_workspace(w.T, dp.p.d_in, dp.p.d_out, bt, flags, device=DEV)
+            agm.fused_linear(dp.base, dp.pool, seg, x, vs[dps.index(dp)], y1, flags=flags, workspace=ws1)
+            torch.cuda.synchronize()
+            assert rel_l2(got, to_f64(y1)) <= tol
+    # base products alone: no pools, no v
+    ys = [torch.full((w.T, dp.p.d_out), float("nan"), device=DEV).to(dp.ydtype) for dp in dps]
+    wsp = agm.fused_slices_workspace(w.T, p0.d_in, d_outs, bt, 0, device=DEV)
+    agm.fused_linear_slices([dp.base for dp in dps], None, seg, x, None, ys, workspace=wsp)
+    torch.cuda.synchronize()
+    live = np.zeros(w.T, bool)
+    for dp, wk, y in zip(dps, ws, ys):
+        args = list(dp.oracle_args(wk)[1:])
+        args[0] = np.full(w.T, -1, np.int32)      # no adapter on any row: the base product
+        ref = oracle.linear(x_host, dp.w0_host, *args)
+        assert rel_l2(to_f64(y), ref) <= _tol(dp.p), (case, dp.p.name, "base only")
+
+
 def test_fused_w8a8_parity():
     w = make_workload("fp8_fused", **SMALL["fp8_fused"])
     p = w.projections[0]
