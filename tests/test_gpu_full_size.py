@@ -20,6 +20,7 @@ import adapter_gemm_amd as agm
 import oracle
 from lora_inputs import make_workload
 from gpu_helpers import DEV, DevProjection, split_seg, rel_l2, row_rel_l2, to_f64
+from bench import SLICE_GROUPS
 
 TOL = {"fp32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
 N_SAMPLE = 64
@@ -40,6 +41,42 @@ def _sample_rows(w, seed=7):
         rows = np.flatnonzero(live & (w.ids == big))
         sel.update([int(rows[0]), int(rows[-1])])
     return np.array(sorted(sel))
+
+
+def _check_slices(w, projs, seg, sel, pos_of_row, n_act):
+    """One sliced launch over projections that share the first one's input."""
+    dps = [DevProjection(w, p) for p in projs]
+    x, x_host = dps[0].x, dps[0].x_host
+    vs = []
+    for dp in dps:
+        v = torch.full((w.T, dp.p.r_cap), float("nan"), device=DEV)
+        agm.shrink(dp.pool, seg, w.T, None, x, v, launch=agm.LAUNCH_PERSISTENT)
+        vs.append(v)
+    ys = [torch.full((w.T, dp.p.d_out), float("nan"), device=DEV).to(dp.ydtype) for dp in dps]
+    wsp = agm.fused_slices_workspace(w.T, dps[0].p.d_in, [dp.p.d_out for dp in dps], agm.BF16, device=DEV)
+    agm.fused_linear_slices([dp.base for dp in dps], [dp.pool for dp in dps], seg, x, vs, ys, workspace=wsp)
+    torch.cuda.synchronize()
+    xs = x_host[sel]
+    ids_s, act_s = w.ids[sel], w.active[sel]
+    live_s = oracle.live_rows(ids_s, act_s)
+    for dp, v, y in zip(dps, vs, ys):
+        p = dp.p
+        args = dp.oracle_args(w)
+        y_ref = oracle.linear(xs, dp.w0_host, ids_s, act_s, *args[3:])
+        got = to_f64(y)[sel]
+        tol = TOL[p.data_dtype]
+        assert np.isfinite(got).all(), p.name
+        assert rel_l2(got, y_ref) <= tol and row_rel_l2(got, y_ref) <= tol, (p.name, rel_l2(got, y_ref))
+        if live_s.any():
+            v_ref = oracle.shrink_rows(xs[live_s], ids_s[live_s], act_s[live_s], dp.A_host, p.slot_rank)
+            pos = pos_of_row[sel[live_s]]
+            assert (pos < n_act).all()
+            vg = v.cpu().numpy().astype(np.float64)[pos]
+            mask = np.arange(p.r_cap)[None, :] < p.slot_rank[ids_s[live_s]][:, None]
+            assert rel_l2(np.where(mask, vg, 0), v_ref) <= TOL["fp32"], p.name
+        print(f"[full-size] {w.name}/{p.name} (sliced launch): rel L2 {rel_l2(got, y_ref):.2e}", flush=True)
+    del dps, vs, ys
+    torch.cuda.empty_cache()
 
 
 def _run_path(w, dp, seg, flags=0):
@@ -76,7 +113,13 @@ def test_full_size_bench_path(name):
     pos_of_row = np.empty(w.T, np.int64)
     pos_of_row[d["perm"]] = np.arange(w.T)
     n_act = ref["n_active"]
-    for p in w.projections:
+    # projections that bench.py runs as one sliced launch on one input
+    names = [p.name for p in w.projections]
+    for grp in SLICE_GROUPS.get(name, [[n] for n in names]):
+        if len(grp) > 1:
+            _check_slices(w, [w.projections[names.index(n)] for n in grp], seg, sel, pos_of_row, n_act)
+            continue
+        p = w.projections[names.index(grp[0])]
         dp = DevProjection(w, p)
         v, y = _run_path(w, dp, seg)
         args = dp.oracle_args(w)
