@@ -73,6 +73,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Workgroup barrier for data exchanged through LDS: waits for this wave's
+// LDS operations only, so global stores still in flight (which no thread of
+// the workgroup reads back) do not hold the barrier as __syncthreads() does.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 128-bit global loads / stores
 __device__ __forceinline__ u32x4_t ld128(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st128(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }

@@ -599,20 +599,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   uint16_t* __restrict__ Y = static_cast<uint16_t*>(a.y);
   if (S_total > 1) {
     // Hand-off without L2-wide fences: partial tiles are written and read
-    // with agent-scope atomic accesses (coherent across XCDs at the memory
-    // side, never left dirty in or read stale from an XCD's L2); every wave
+    // 16 bytes per lane with device-coherent (sc1) buffer accesses, which
+    // are never left dirty in or read stale from an XCD's L2; every wave
     // drains its stores (vmcnt(0)) before the barrier that precedes the
     // counter increment, and the reads are issued only after the increment
     // that found all other partials counted.
-    float* mine = a.part + ((size_t)tile * S_total + split) * (BM * BN) + (size_t)wave * TM * TN * 256;
+    constexpr int kSc1 = 16;                     // cache-policy bits: sc1
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, 0x7fffffff, kBufferWord3);
+    const uint32_t wave_off = (uint32_t)(wave * TM * TN * 256) * 4u;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __hip_atomic_store(mine + ((i * TN + j) * 64 + lane) * 4 + e, acc[i][j][e], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            acc[i][j], prs, wave_off + (uint32_t)(((i * TN + j) * 64 + lane) * 16),
+            (int)(((uint32_t)(tile * S_total + split) * (BM * BN)) * 4u), kSc1);
     vm_barrier<0>();
     if (tid == 0)
       s_flag = __hip_atomic_fetch_add(&a.counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S_total - 1;
@@ -623,15 +624,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S_total; ++s) {
-      const float* src = a.part + ((size_t)tile * S_total + s) * (BM * BN) + (size_t)wave * TM * TN * 256;
+      const int soff = (int)(((uint32_t)(tile * S_total + s) * (BM * BN)) * 4u);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[i][j][e] += __hip_atomic_load(src + ((i * TN + j) * 64 + lane) * 4 + e, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+          acc[i][j] += __builtin_amdgcn_raw_buffer_load_b128(
+              prs, wave_off + (uint32_t)(((i * TN + j) * 64 + lane) * 16), soff, kSc1);
     }
     if (tid == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

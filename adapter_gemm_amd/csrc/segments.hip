@@ -55,7 +55,7 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_incl_sum(v);
   if (lane == 63) wave_sums[wave] = incl;
-  __syncthreads();
+  lds_sync();
   int before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -64,7 +64,7 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
     all += t;
   }
   *total = all;
-  __syncthreads();
+  lds_sync();
   return before + incl - v;
 }
 
@@ -76,7 +76,7 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* wave_sums, int4* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int4 incl = make_int4(wave_incl_sum(v.x), wave_incl_sum(v.y), wave_incl_sum(v.z), wave_incl_sum(v.w));
   if (lane == 63) wave_sums[wave] = incl;
-  __syncthreads();
+  lds_sync();
   int4 before = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -85,7 +85,7 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* wave_sums, int4* total) {
     all.x += t.x; all.y += t.y; all.z += t.z; all.w += t.w;
   }
   *total = all;
-  __syncthreads();
+  lds_sync();
   return make_int4(before.x + incl.x - v.x, before.y + incl.y - v.y, before.z + incl.z - v.z,
                    before.w + incl.w - v.w);
 }
@@ -126,7 +126,7 @@ __device__ void build_order1_segments(int N, int* cnt, const int* sidx, int* sst
       atomicMax(&sh.mmax, cnt[a]);
     }
   }
-  __syncthreads();
+  lds_sync();
 
   // segment starts and row tiles
   {
@@ -163,7 +163,7 @@ __device__ void build_order1_segments(int N, int* cnt, const int* sidx, int* sst
       P.sum[kNTilesLarge] = run_l;
     }
   }
-  __syncthreads();
+  lds_sync();
 
   // placement cursor per adapter = start of its segment
   for (int a = tid; a < N; a += THREADS)
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
     sidx[a] = (order == 1) ? 0x7fffffff : 0;
   }
   if (tid == 0) { sh.err = 0; sh.mmax = 0; sh.dead_run = 0; }
-  __syncthreads();
+  lds_sync();
 
   // 1. histogram by runs, validation, first appearance.  A batch of at most
   // THREADS rows is one chunk: its ids, live flags and runs stay in registers
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
       if (single) { r_id = id; r_live = live; r_rank = rank; r_leader = leader; r_run = run; }
     }
   }
-  __syncthreads();
+  lds_sync();
   if (sh.err) {
     if (tid == 0) {
       for (int w = 0; w < kSegHeader; ++w) P.sum[w] = 0;
@@ -281,14 +281,14 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
       if (first) sidx[id] = -(run + ex) - 1;
       run += tot;
     }
-    __syncthreads();
+    lds_sync();
     for (int a = tid; a < N; a += THREADS)
       if (cnt[a] > 0) sidx[a] = -sidx[a] - 1;
     if (tid == 0) sh.nseg = run;
-    __syncthreads();
+    lds_sync();
     build_order1_segments<THREADS>(N, cnt, sidx, sst, P, sh);
   }
-  __syncthreads();
+  lds_sync();
   const int S = sh.nseg;
 
 
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
         cnt[id] = b + run;
         sh.run_base[wave][lane] = b;
       }
-      __syncthreads();
+      lds_sync();
     }
     int dead_before = sh.dead_run;
     for (int w = 0; w < wave; ++w) dead_before += sh.wave_dead[w];
@@ -331,13 +331,13 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
       P.perm[pos] = i;
       P.pos_seg[pos] = live ? sidx[id] : -1;
     }
-    __syncthreads();
+    lds_sync();
     if (tid == 0) {
       int d = 0;
       for (int w = 0; w < kWaves; ++w) d += sh.wave_dead[w];
       sh.dead_run += d;
     }
-    __syncthreads();
+    lds_sync();
   }
 
   // 4. summary; R = min{r in {16*2^k < T} U {T} : r >= m_max}

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     // acc[e] = partial product[row = 4 * (lane / 16) + e][col = lane % 16];
     // v[s, c] is the sum over slices q of product[s + Pw q][c + Pw q]
     red[wave][lane] = acc;
-    __syncthreads();
+    lds_sync();
     if (threadIdx.x < 256) {
       const int t = threadIdx.x;              // one output each, slices and waves summed in order
       const int row = t >> 4, col = t & 15;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
       }
       if (row < w.rows && col < jn) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + col] = s;
     }
-    __syncthreads();
+    lds_sync();
   }
 }
 
