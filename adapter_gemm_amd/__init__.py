@@ -28,6 +28,8 @@ EXPORTED = [
     "lora_segment_words", "lora_build_segments", "lora_plan_segments", "lora_build_segments_dev",
     "lora_shrink", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
     "lora_fused_linear_slices", "lora_fused_slices_workspace_bytes",
+    "lora_registry_create", "lora_registry_destroy", "lora_registry_acquire", "lora_registry_release",
+    "lora_registry_lookup", "lora_registry_stats", "lora_pool_install",
     "lora_quantize_e4m3", "lora_status_string", "lora_last_error",
 ]
 
@@ -80,6 +82,13 @@ def _load():
         "lora_fused_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "lora_fused_linear_slices": (I32, [I32, P, P, P, I32, P, I32, I32, P, P, P, P, P, I32, P, SZ, P]),
         "lora_fused_slices_workspace_bytes": (SZ, [I32, I32, I32, P, I32, I32]),
+        "lora_registry_create": (I32, [I32, I32, P]),
+        "lora_registry_destroy": (None, [P]),
+        "lora_registry_acquire": (I32, [P, ctypes.c_int64, P, P]),
+        "lora_registry_release": (I32, [P, ctypes.c_int64]),
+        "lora_registry_lookup": (I32, [P, ctypes.c_int64, P]),
+        "lora_registry_stats": (I32, [P, P]),
+        "lora_pool_install": (I32, [P, I32, P, P, I32, ctypes.c_float, P]),
         "lora_quantize_e4m3": (I32, [P, I32, I32, I32, P, I32, P, P]),
         "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lora_last_error": (ctypes.c_char_p, []),
@@ -129,13 +138,17 @@ def pool_desc(A, B, slot_rank, slot_scale) -> PoolDesc:
     slot_scale fp32 [N], all on the device."""
     N, r_cap, d_in = A.shape
     d_out = B.shape[1]
-    return PoolDesc(A.data_ptr(), B.data_ptr(), slot_rank.data_ptr(), slot_scale.data_ptr(), _dtype_code(A),
-                    N, r_cap, d_in, d_out)
+    d = PoolDesc(A.data_ptr(), B.data_ptr(), slot_rank.data_ptr(), slot_scale.data_ptr(), _dtype_code(A),
+                 N, r_cap, d_in, d_out)
+    d._keep = (A, B, slot_rank, slot_scale)   # the descriptor holds raw addresses: keep their memory alive
+    return d
 
 
 def base_desc(W, w_scale=None) -> BaseDesc:
     """W [d_out, ld_w] fp32 / bf16 / uint8 e4m3 codes; w_scale fp32 [d_out] for fp8."""
-    return BaseDesc(W.data_ptr(), _ptr(w_scale), _dtype_code(W), W.stride(0))
+    d = BaseDesc(W.data_ptr(), _ptr(w_scale), _dtype_code(W), W.stride(0))
+    d._keep = (W, w_scale)
+    return d
 
 
 def segment_words(T: int) -> int:
@@ -196,6 +209,59 @@ def fused_workspace(T: int, d_in: int, d_out: int, base_dtype: int, flags: int =
     import torch
     n = fused_workspace_bytes(T, d_in, d_out, base_dtype, flags)
     return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+EVICT_LRU, EVICT_LFU = 0, 1
+
+
+class Registry:
+    """Adapter residency over the slots of a pool (host bookkeeping in the
+    library): adapters are named by any hashable; acquire() returns the slot
+    and whether it must be filled (pool_install) before kernels read it."""
+
+    def __init__(self, n_slots: int, policy: int = EVICT_LRU):
+        h = ctypes.c_void_p()
+        _check(_lib.lora_registry_create(n_slots, policy, ctypes.byref(h)), "lora_registry_create")
+        self._h = h
+        self._destroy = _lib.lora_registry_destroy      # kept: module globals may be gone at exit
+        self._keys = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+            self._h = None
+
+    def _key(self, name) -> int:
+        return self._keys.setdefault(name, len(self._keys))
+
+    def acquire(self, name):
+        """(slot, needs_install) for one use of `name`; raises LoraError with
+        LORA_E_SIZE when every slot holds an adapter in use."""
+        slot, need = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.lora_registry_acquire(self._h, self._key(name), ctypes.byref(slot), ctypes.byref(need)),
+               "lora_registry_acquire")
+        return int(slot.value), bool(need.value)
+
+    def release(self, name) -> None:
+        _check(_lib.lora_registry_release(self._h, self._key(name)), "lora_registry_release")
+
+    def lookup(self, name) -> int:
+        slot = ctypes.c_int32()
+        _check(_lib.lora_registry_lookup(self._h, self._key(name), ctypes.byref(slot)), "lora_registry_lookup")
+        return int(slot.value)
+
+    def stats(self) -> dict:
+        out = (ctypes.c_int64 * 4)()
+        _check(_lib.lora_registry_stats(self._h, out), "lora_registry_stats")
+        return {"hits": out[0], "misses": out[1], "evictions": out[2], "resident": out[3]}
+
+
+def pool_install(pool: PoolDesc, slot: int, A, B, rank: int, scale: float, stream=None) -> None:
+    """Fill one slot: A [rank, d_in], B [d_out, rank] (host, ideally pinned, or
+    device tensors in the pool dtype), asynchronously on the stream."""
+    _check(_lib.lora_pool_install(ctypes.byref(pool), slot, _ptr(A), _ptr(B), rank, scale, _stream(stream)),
+           "lora_pool_install")
 
 
 def fused_slices_workspace(T: int, d_in: int, d_outs, base_dtype: int, flags: int = 0, device="cuda"):

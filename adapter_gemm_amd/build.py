@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["lora_api.cpp", "segments.hip", "shrink.hip", "expand.hip", "fused_linear.hip", "fused_dma.hip", "quant.hip"]
+SOURCES = ["lora_api.cpp", "registry.cpp", "segments.hip", "shrink.hip", "expand.hip", "fused_linear.hip", "fused_dma.hip",
+           "quant.hip", "residency.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

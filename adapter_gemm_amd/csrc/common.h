@@ -152,6 +152,8 @@ hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const 
 size_t fused_quant_bytes(int T, int d_in, int flags, int base_dtype);
 size_t fused_workspace_bytes(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap);
 
+hipError_t launch_pool_install(const lora_pool_t& pool, int slot, const void* A, const void* B, int rank,
+                               float scale, hipStream_t st);
 hipError_t launch_quantize_e4m3(const void* x, int T, int d, int ld_x, uint8_t* q, int ld_q, float* s_x,
                                 hipStream_t st);
 

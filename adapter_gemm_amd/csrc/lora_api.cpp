@@ -313,6 +313,15 @@ int lora_fused_linear_slices(int32_t n_slices, const lora_base_t* bases, const l
                                               flags, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int lora_pool_install(const lora_pool_t* pool, int32_t slot, const void* A, const void* B, int32_t rank,
+                      float scale, void* stream) {
+  const int st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (slot < 0 || slot >= pool->n_slots || rank < 0 || rank > pool->r_cap) return LORA_E_ARG;
+  if (rank > 0 && (!A || !B)) return LORA_E_ARG;
+  return hip_status(lora::launch_pool_install(*pool, slot, A, B, rank, scale, static_cast<hipStream_t>(stream)));
+}
+
 int lora_quantize_e4m3(const void* x, int32_t T, int32_t d, int32_t ld_x, uint8_t* q, int32_t ld_q, float* s_x,
                        void* stream) {
   if (T < 0 || d < 0 || (T > 0 && (!x || !q || !s_x))) return LORA_E_ARG;

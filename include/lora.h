@@ -30,7 +30,8 @@
  * --------------------------------
  * Memory.  Every buffer is owned by the caller.  "device" pointers are HIP
  *   device memory of the current device; "host" pointers are ordinary host
- *   memory.  The library allocates nothing and keeps no device state.
+ *   memory.  The library allocates no device memory and keeps no device
+ *   state; a registry handle owns only host memory.
  * Streams.  Every call is asynchronous on the given hipStream_t (passed as
  *   void*; NULL = the null stream).  No call synchronises the stream or reads
  *   device memory back to the host.
@@ -288,6 +289,57 @@ int lora_fused_linear_slices(int32_t n_slices, const lora_base_t* bases, const l
 /* Workspace bytes lora_fused_linear_slices needs for this call shape. */
 size_t lora_fused_slices_workspace_bytes(int32_t n_slices, int32_t T, int32_t d_in, const int32_t* d_out,
                                          int32_t base_dtype, int32_t flags);
+
+/* ---- adapter residency ------------------------------------------------ */
+/*
+ * A pool holds n_slots adapters at a time; an adapter registry decides which
+ * adapter occupies which slot ("LLM-stack book" 7.14.4: a registry maps an
+ * adapter to its slot, counts the batches in flight that use it, and when a
+ * new adapter needs a slot evicts a resident one that no batch uses, by
+ * least-recent use, or by fewest uses in the LFU variant).  The registry is
+ * host bookkeeping (host memory owned by the handle, not thread-safe: one
+ * host thread per registry); lora_pool_install moves the weights.
+ */
+#define LORA_EVICT_LRU 0
+#define LORA_EVICT_LFU 1
+typedef struct lora_registry lora_registry_t;
+
+/* New registry over slots 0 .. n_slots-1, all free.  Errors: LORA_E_ARG. */
+int lora_registry_create(int32_t n_slots, int32_t policy, lora_registry_t** out);
+void lora_registry_destroy(lora_registry_t* registry);
+
+/* One batch's use of adapter `key` (any id >= 0 the caller chooses).
+ * Resident: *slot is its slot, *needs_install = 0.  Not resident: it takes
+ * the lowest free slot, else evicts the policy's victim among slots whose
+ * use count is zero; *needs_install = 1 and the caller must fill the slot
+ * (lora_pool_install) before kernels read it.  Either way the slot's use
+ * count goes up by one.  LORA_E_SIZE if every slot holds an adapter in use
+ * (nothing changes).  LRU victim: oldest last acquire; LFU: fewest acquires
+ * over the registry's life, ties by oldest last acquire. */
+int lora_registry_acquire(lora_registry_t* registry, int64_t key, int32_t* slot, int32_t* needs_install);
+/* End of one use (the batch's kernels are done with the slot).  LORA_E_ARG
+ * if `key` is not resident or has no use to end. */
+int lora_registry_release(lora_registry_t* registry, int64_t key);
+/* *slot = the slot of `key`, or -1 if it is not resident. */
+int lora_registry_lookup(const lora_registry_t* registry, int64_t key, int32_t* slot);
+/* out4 = {hits, misses, evictions, resident adapters}. */
+int lora_registry_stats(const lora_registry_t* registry, int64_t* out4);
+
+/*
+ * Fill pool slot `slot` with one adapter ("LLM-stack book" 7.14.3): A
+ * [rank, d_in] and B [d_out, rank] in the pool dtype, host or device memory,
+ * row-major and contiguous; rank 0 .. r_cap; scale = s_a.  Asynchronous on
+ * `stream`: host sources should be pinned (hipHostMalloc) for the copy to be
+ * asynchronous and must stay untouched until the stream has passed the call.
+ * The slot's rank and scale are written by a kernel on the same stream, after
+ * the weights, so a graph can capture the call.  Kernels that read the slot
+ * must be ordered after it (same stream, or an event).  Entries past `rank`
+ * are left as they were (kernels never read them).
+ * Errors: as the pool checks of lora_shrink; LORA_E_ARG for a slot or rank
+ * out of range or a NULL source with rank > 0.
+ */
+int lora_pool_install(const lora_pool_t* pool, int32_t slot, const void* A, const void* B, int32_t rank,
+                      float scale, void* stream);
 
 /*
  * Per-token activation quantisation for the W8A8 base product ("EpiLoRA" 2

@@ -12,8 +12,8 @@ bf16 data is drawn in fp32 and rounded to bf16 (round to nearest even) here,
 fp8 base weights are quantised here to OCP e4m3 codes plus per-output-channel
 fp32 scales.  Both oracle and kernels read the stored values.
 
-Shapes, distributions and id/mask/length recipes follow the five workloads
-described in DESIGN.md (the "input recipe" section).
+Shapes, distributions and id/mask/length recipes of the five workloads
+(``CONFIG_NAMES``) are stated where each is built, in ``make_workload``.
 """
 from __future__ import annotations
 

@@ -14,6 +14,8 @@ grouping and its own launch-geometry formulas, written from the pages:
   and Algorithm 1, 3.2 adapter release);
 * "EpiLoRA: Fusing Many LoRA Adapters into Low-Precision GEMMs" (2, Fig. 4:
   the per-token quantised FP8 projection y = (x_q W_q^T) s_x s_w; 3.1 K1/K2);
+* the same book's 7.14.3-7.14.4 (hot-swapping, the adapter registry and its
+  LRU / LFU eviction) for the slot residency rules;
 * "LoRAForge" (2 Multi-LoRA Serving: Z = X A^T then the expand; 4.1 retained
   ranks below the pool capacity).
 
@@ -28,6 +30,7 @@ from .layer import (live_rows, base_output, shrink_rows, lora_delta, lora_delta_
 from .segments import build_segments, row_tiles
 from .launch import (row_bound_set, row_bound, tiles_full_batch, tiles_shared_bound,
                      tiles_two_class, tiles_exact, class_separation_enabled)
+from .residency import Residency
 
 __all__ = [
     "decode_bf16", "decode_e4m3", "encode_e4m3", "E4M3_MAX",
@@ -35,5 +38,5 @@ __all__ = [
     "lora_delta_gathered", "linear", "merged_linear", "act_quant_e4m3", "linear_w8a8",
     "build_segments", "row_tiles",
     "row_bound_set", "row_bound", "tiles_full_batch", "tiles_shared_bound", "tiles_two_class",
-    "tiles_exact", "class_separation_enabled",
+    "tiles_exact", "class_separation_enabled", "Residency",
 ]

@@ -236,3 +236,67 @@ def test_fused_slices_host_checks():
     ys2 = (ctypes.c_void_p * 2)(2 * fake, 2 * fake)
     assert lib.lora_fused_linear_slices(2, same, None, None, 8, fake, 64, 64, dd, None, None, ys2, ldy, 0,
                                         None, 0, None) == E_ARG
+
+
+@pytest.mark.parametrize("policy", [0, 1])
+def test_registry_matches_the_residency_rules(policy):
+    """The library's registry and the oracle's residency rules take the same
+    slot, install and eviction decisions over 3000 acquires and releases of a
+    few hot adapters and a long tail, including refusals when every slot is in
+    use."""
+    rng = np.random.default_rng(11 + policy)
+    n = 5
+    reg = agm.Registry(n, policy)
+    model = oracle.Residency(n, "lfu" if policy == 1 else "lru")
+    held = []
+    for step in range(3000):
+        if held and rng.random() < 0.45:
+            k = held.pop(int(rng.integers(len(held))))
+            reg.release(k)
+            assert model.release(k)
+            continue
+        k = int(min(rng.zipf(1.3), 12))              # a few hot adapters, a long tail
+        want = model.acquire(k)
+        if want is None:
+            with pytest.raises(agm.LoraError):
+                reg.acquire(k)
+            continue
+        assert reg.acquire(k) == want, (step, k)
+        held.append(k)
+        assert reg.lookup(k) == want[0]
+    st = reg.stats()
+    assert [st["hits"], st["misses"], st["evictions"]] == [model.hits, model.misses, model.evictions]
+    assert st["resident"] == model.resident()
+    with pytest.raises(agm.LoraError):
+        reg.release(10**6)                           # never acquired
+
+
+def test_registry_and_install_argument_errors():
+    lib = agm.lib()
+    h = ctypes.c_void_p()
+    assert lib.lora_registry_create(0, 0, ctypes.byref(h)) == 1
+    assert lib.lora_registry_create(4, 7, ctypes.byref(h)) == 1
+    assert lib.lora_pool_install(None, 0, None, None, 0, 1.0, None) == 1
+
+
+def test_descriptors_keep_their_tensors_alive():
+    """A descriptor carries raw addresses into the library, so it must hold its
+    tensors: a weight built inline (``base_desc(make())``) freed at once would
+    hand its memory to the next allocation while the descriptor still points
+    at it."""
+    import gc
+    import weakref
+    import torch
+    W = torch.zeros(8, 16, dtype=torch.bfloat16)
+    ref = weakref.ref(W)
+    d = agm.base_desc(W)
+    del W
+    gc.collect()
+    assert ref() is not None and d.W == ref().data_ptr()
+    A = torch.zeros(2, 4, 16, dtype=torch.bfloat16)
+    refs = [weakref.ref(t) for t in (A,)]
+    p = agm.pool_desc(A, torch.zeros(2, 8, 4, dtype=torch.bfloat16), torch.zeros(2, dtype=torch.int32),
+                      torch.zeros(2))
+    del A
+    gc.collect()
+    assert all(r() is not None for r in refs) and p.A == refs[0]().data_ptr()

@@ -338,6 +338,68 @@ def test_fused_slices_parity(case):
         assert rel_l2(to_f64(y), ref) <= _tol(dp.p), (case, dp.p.name, "base only")
 
 
+# ---- adapter residency: registry + slot installs ----------------------------------
+
+def test_residency_install_and_evict():
+    """Twelve adapters served through a five-slot pool: each batch acquires
+    its adapters from the registry, the misses are installed from pinned host
+    memory on a side stream, the compute stream waits for that copy, and the
+    fused output matches the oracle on the adapters' own ids (the pool starts
+    as NaN, so a slot read before its install would poison the output)."""
+    from lora_inputs import bf16_round
+    g = np.random.default_rng(21)
+    n_ad, n_slots, r_cap, d_in, d_out, T = 12, 5, 16, 256, 136, 96
+    ranks = g.integers(1, r_cap + 1, n_ad).astype(np.int32)
+    scales = g.uniform(0.5, 2.0, n_ad).astype(np.float32)
+    A_all = np.zeros((n_ad, r_cap, d_in), np.uint16)
+    B_all = np.zeros((n_ad, d_out, r_cap), np.uint16)
+    A_src, B_src = [], []
+    for k in range(n_ad):
+        a = bf16_round(g.standard_normal((ranks[k], d_in)).astype(np.float32) * 0.05)
+        b = bf16_round(g.standard_normal((d_out, ranks[k])).astype(np.float32) * 0.05)
+        A_all[k, :ranks[k]] = a
+        B_all[k, :, :ranks[k]] = b
+        A_src.append(torch.from_numpy(a.view(np.int16)).pin_memory())
+        B_src.append(torch.from_numpy(b.view(np.int16)).pin_memory())
+    W0 = bf16_round(g.standard_normal((d_out, d_in)).astype(np.float32) * 0.02)
+    base = agm.base_desc(bf16_dev(W0))
+    A_pool = torch.full((n_slots, r_cap, d_in), float("nan"), device=DEV).to(torch.bfloat16)
+    B_pool = torch.full((n_slots, d_out, r_cap), float("nan"), device=DEV).to(torch.bfloat16)
+    rank_d = torch.zeros(n_slots, dtype=torch.int32, device=DEV)
+    scale_d = torch.zeros(n_slots, dtype=torch.float32, device=DEV)
+    pool = agm.pool_desc(A_pool, B_pool, rank_d, scale_d)
+    reg = agm.Registry(n_slots, agm.EVICT_LRU)
+    copy = torch.cuda.Stream()
+    ws = agm.fused_workspace(T, d_in, d_out, agm.BF16, device=DEV)
+    for names in ([0, 1, 2], [3, 1, 4, 5, 6], [0, 7, 8], [9, 10, 11, 2, 3], [1, 0]):
+        ids_ad = g.choice(names + [-1], size=T).astype(np.int32)
+        slot_of = {}
+        for k in sorted(set(ids_ad[ids_ad >= 0].tolist())):
+            s_, need = reg.acquire(k)
+            slot_of[k] = s_
+            if need:
+                agm.pool_install(pool, s_, A_src[k], B_src[k], int(ranks[k]), float(scales[k]), stream=copy)
+        torch.cuda.current_stream().wait_event(copy.record_event())
+        ids_slot = np.array([slot_of[k] if k >= 0 else -1 for k in ids_ad], np.int32)
+        x_h = bf16_round(g.standard_normal((T, d_in)).astype(np.float32))
+        x = bf16_dev(x_h)
+        seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=DEV)
+        agm.build_segments_dev(torch.from_numpy(ids_slot).to(DEV), None, n_slots, seg)
+        v = torch.zeros(T, r_cap, device=DEV)
+        agm.shrink(pool, seg, T, None, x, v, launch=agm.LAUNCH_PERSISTENT)
+        y = torch.full((T, d_out), float("nan"), device=DEV).to(torch.bfloat16)
+        agm.fused_linear(base, pool, seg, x, v, y, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.linear(x_h, W0, ids_ad, np.ones(T, np.uint8), A_all, B_all, ranks, scales)
+        got = to_f64(y)
+        assert np.isfinite(got).all(), names
+        assert rel_l2(got, ref) <= TOL["bf16"] and row_rel_l2(got, ref) <= TOL["bf16"], names
+        for k in slot_of:
+            reg.release(k)
+    st = reg.stats()
+    assert st["evictions"] > 0 and st["hits"] > 0
+
+
 def test_fused_w8a8_parity():
     w = make_workload("fp8_fused", **SMALL["fp8_fused"])
     p = w.projections[0]
