@@ -47,6 +47,19 @@ __device__ __forceinline__ int wave_incl_sum(int v) {
   return v;
 }
 
+// Maximum over the 64 lanes of a wave of values >= 0, in lane 63 (the same
+// shifts as the sum; a disabled DPP source reads as 0).  Every lane of the
+// wave must take part.
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 // Exclusive prefix sum of one value per thread over the workgroup; the total
 // is written to *total for every thread.
 template <int THREADS>
@@ -100,7 +113,7 @@ __device__ __forceinline__ int wave_runs(bool live, int id, int lane, int& leade
   run = 0;
   while (remaining) {
     const int l = __ffsll((unsigned long long)remaining) - 1;
-    const int key = __shfl(id, l, 64);
+    const int key = __builtin_amdgcn_readlane(id, l);   // l is wave-uniform: a VALU lane read, no LDS trip
     const uint64_t m = __ballot(live && id == key);
     if (live && id == key) {
       rank = __popcll(m & lanemask_lt());
@@ -119,13 +132,18 @@ template <int THREADS>
 __device__ void build_order1_segments(int N, int* cnt, const int* sidx, int* sst, const SegPtrs& P, BuildLds& sh) {
   const int tid = threadIdx.x;
   const int S = sh.nseg;
-  for (int a = tid; a < N; a += THREADS) {
-    if (cnt[a] > 0) {
-      sst[sidx[a]] = cnt[a];
+  int mx = 0;
+  for (int base = 0; base < N; base += THREADS) {
+    const int a = base + tid;
+    const int c = a < N ? cnt[a] : 0;
+    if (c > 0) {
+      sst[sidx[a]] = c;
       P.seg_adapter[sidx[a]] = a;
-      atomicMax(&sh.mmax, cnt[a]);
     }
+    mx = max(mx, c);
   }
+  mx = wave_max_nonneg(mx);
+  if ((tid & 63) == 63 && mx > 0) atomicMax(&sh.mmax, mx);
   lds_sync();
 
   // segment starts and row tiles
@@ -170,6 +188,53 @@ __device__ void build_order1_segments(int N, int* cnt, const int* sidx, int* sst
     if (cnt[a] > 0) cnt[a] = sst[sidx[a]];
 }
 
+// Canonical order (ascending adapter id): segment index, start and row-tile
+// offsets of every present adapter are one four-field prefix sum over the
+// adapters; cnt[a] (rows of a) becomes a's placement cursor.  Sets sh.nseg,
+// sh.nact, sh.mmax and the tile counts of the summary.
+template <int THREADS>
+__device__ void canonical_segments(int N, int* cnt, int* sidx, const SegPtrs& P, BuildLds& sh) {
+  const int tid = threadIdx.x;
+  int4 run = make_int4(0, 0, 0, 0);
+  int mx = 0;
+  for (int base = 0; base < N; base += THREADS) {
+    const int a = base + tid;
+    const int len = a < N ? cnt[a] : 0;
+    const int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
+    const int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
+    int4 tot;
+    const int4 ex = block_exclusive_scan4<THREADS>(make_int4(len > 0, len, ns, nl), sh.wave_sums4, &tot);
+    if (len > 0) {
+      const int sg = run.x + ex.x, st = run.y + ex.y, os = run.z + ex.z, ol = run.w + ex.w;
+      sidx[a] = sg;
+      P.seg_adapter[sg] = a;
+      P.seg_start[sg] = st;
+      for (int t = 0; t < ns; ++t) {
+        P.tiles_small[2 * (os + t)] = st + t * LORA_TILE_SMALL;
+        P.tiles_small[2 * (os + t) + 1] = sg;
+      }
+      for (int t = 0; t < nl; ++t) {
+        P.tiles_large[2 * (ol + t)] = st + t * LORA_TILE_LARGE;
+        P.tiles_large[2 * (ol + t) + 1] = sg;
+      }
+      cnt[a] = st;
+    }
+    mx = max(mx, len);
+    run.x += tot.x; run.y += tot.y; run.z += tot.z; run.w += tot.w;
+  }
+  // m_max: one wave maximum and one LDS atomic per wave (a per-lane atomic on
+  // one address becomes a serial loop over the lanes)
+  mx = wave_max_nonneg(mx);
+  if ((tid & 63) == 63 && mx > 0) atomicMax(&sh.mmax, mx);
+  if (tid == 0) {
+    sh.nseg = run.x;
+    sh.nact = run.y;
+    P.seg_start[run.x] = run.y;
+    P.sum[kNTilesSmall] = run.z;
+    P.sum[kNTilesLarge] = run.w;
+  }
+}
+
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* __restrict__ ids,
                                                                  const uint8_t* __restrict__ active, int T, int N,
@@ -185,6 +250,12 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
   const int lane = tid & 63, wave = tid >> 6;
   SegPtrs P = seg_ptrs(seg, T);
 
+  // the first chunk's ids and flags are loaded together, before the LDS set-up
+  int id0 = -1, on0 = 1;
+  if (tid < T) {
+    id0 = ids[tid];
+    if (active != nullptr) on0 = active[tid];
+  }
   for (int a = tid; a < N; a += THREADS) {
     cnt[a] = 0;
     sidx[a] = (order == 1) ? 0x7fffffff : 0;
@@ -203,9 +274,14 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
     int id = -1;
     bool live = false;
     if (i < T) {
-      id = ids[i];
+      bool on = on0 != 0;
+      id = id0;
+      if (base > 0) {
+        id = ids[i];
+        on = active == nullptr || active[i] != 0;   // both loads in flight together
+      }
       if (id < -1 || id >= N) sh.err = 1;
-      else live = id >= 0 && (active == nullptr || active[i] != 0);
+      else live = id >= 0 && on;
     }
     if (base + wave * 64 < T) {
       int leader, run;
@@ -229,41 +305,7 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
 
   // 2. segments
   if (order == 0) {
-    // adapters in ascending id: segment index, start and tile offsets are
-    // prefix sums over the adapters; cnt becomes the placement cursor
-    int4 run = make_int4(0, 0, 0, 0);
-    for (int base = 0; base < N; base += THREADS) {
-      const int a = base + tid;
-      const int len = a < N ? cnt[a] : 0;
-      const int ns = (len + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
-      const int nl = (len + LORA_TILE_LARGE - 1) / LORA_TILE_LARGE;
-      int4 tot;
-      const int4 ex = block_exclusive_scan4<THREADS>(make_int4(len > 0, len, ns, nl), sh.wave_sums4, &tot);
-      if (len > 0) {
-        const int sg = run.x + ex.x, st = run.y + ex.y, os = run.z + ex.z, ol = run.w + ex.w;
-        sidx[a] = sg;
-        P.seg_adapter[sg] = a;
-        P.seg_start[sg] = st;
-        for (int t = 0; t < ns; ++t) {
-          P.tiles_small[2 * (os + t)] = st + t * LORA_TILE_SMALL;
-          P.tiles_small[2 * (os + t) + 1] = sg;
-        }
-        for (int t = 0; t < nl; ++t) {
-          P.tiles_large[2 * (ol + t)] = st + t * LORA_TILE_LARGE;
-          P.tiles_large[2 * (ol + t) + 1] = sg;
-        }
-        cnt[a] = st;
-        atomicMax(&sh.mmax, len);
-      }
-      run.x += tot.x; run.y += tot.y; run.z += tot.z; run.w += tot.w;
-    }
-    if (tid == 0) {
-      sh.nseg = run.x;
-      sh.nact = run.y;
-      P.seg_start[run.x] = run.y;
-      P.sum[kNTilesSmall] = run.z;
-      P.sum[kNTilesLarge] = run.w;
-    }
+    canonical_segments<THREADS>(N, cnt, sidx, P, sh);
   } else {
     // rows that are the first appearance of their adapter, in batch order;
     // indices are stored negated so that a later row never matches
@@ -273,7 +315,8 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
       int id = -1, first = 0;
       if (i < T) {
         id = ids[i];
-        const bool live = id >= 0 && (active == nullptr || active[i] != 0);
+        const bool on = active == nullptr || active[i] != 0;
+        const bool live = id >= 0 && on;
         first = (live && sidx[id] == i) ? 1 : 0;
       }
       int tot;
@@ -303,7 +346,8 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
       live = false;
       if (i < T) {
         id = ids[i];
-        live = id >= 0 && (active == nullptr || active[i] != 0);
+        const bool on = active == nullptr || active[i] != 0;
+        live = id >= 0 && on;
       }
       leader = -1;
       run = 0;
@@ -359,6 +403,121 @@ __global__ __launch_bounds__(THREADS) void build_segments_kernel(const int32_t* 
   }
 }
 
+// Batches of at most 256 rows and pools of at most kSmallMaxSlots adapters:
+// per-wave lane masks instead of a loop over distinct ids.  Each live lane
+// sets its bit in tbl[wave][id] (a 64-bit LDS OR) and reads the word back:
+// its rank among the wave's rows of that id is the popcount of the lower
+// lanes, the lowest set lane leads the run.  A row's place in its segment is
+// the segment start plus the rows of its id in earlier waves (their words)
+// plus its rank, so rows stay in batch order inside every segment.
+constexpr int kSmallRows = 256;
+constexpr int kSmallMaxSlots = 1024;   // 4 waves x N x 8 bytes of masks
+
+__global__ __launch_bounds__(kSmallRows) void build_segments_small_kernel(const int32_t* __restrict__ ids,
+                                                                          const uint8_t* __restrict__ active, int T,
+                                                                          int N, int order,
+                                                                          int32_t* __restrict__ seg) {
+  constexpr int kWaves = kSmallRows / 64;
+  extern __shared__ __attribute__((aligned(16))) uint64_t tbl[];   // [kWaves][N] lane masks
+  int* cnt = reinterpret_cast<int*>(tbl + kWaves * N);              // [N] rows, then placement cursor
+  int* sidx = cnt + N;                                              // [N] segment index per adapter
+  int* sst = sidx + N;                                              // [N] first appearance: lengths/starts
+  __shared__ BuildLds sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  SegPtrs P = seg_ptrs(seg, T);
+
+  int id = -1, on = 1;
+  if (tid < T) {
+    id = ids[tid];
+    if (active != nullptr) on = active[tid];
+  }
+  for (int a = tid; a < N; a += kSmallRows) {
+    cnt[a] = 0;
+    sidx[a] = (order == 1) ? 0x7fffffff : 0;
+  }
+  for (int q = tid; q < kWaves * N; q += kSmallRows) tbl[q] = 0ull;
+  if (tid == 0) { sh.err = 0; sh.mmax = 0; }
+  lds_sync();
+
+  // 1. masks, histogram, validation, first appearance
+  bool live = false;
+  if (tid < T) {
+    if (id < -1 || id >= N) sh.err = 1;
+    else live = id >= 0 && on != 0;
+  }
+  uint64_t* mine = tbl + wave * N;
+  if (live) atomicOr(reinterpret_cast<unsigned long long*>(&mine[id]), 1ull << lane);
+  lds_sync();
+  const uint64_t m = live ? mine[id] : 0ull;
+  if (live && lane == __ffsll((unsigned long long)m) - 1) {
+    atomicAdd(&cnt[id], __popcll(m));
+    if (order == 1) atomicMin(&sidx[id], tid);
+  }
+  lds_sync();
+  if (sh.err) {
+    if (tid == 0) {
+      for (int w = 0; w < kSegHeader; ++w) P.sum[w] = 0;
+      P.sum[kRows] = T;
+      P.sum[kError] = LORA_E_ID;
+    }
+    return;
+  }
+
+  // 2. segments
+  if (order == 0) {
+    canonical_segments<kSmallRows>(N, cnt, sidx, P, sh);
+  } else {
+    // rows that are the first appearance of their adapter, in batch order
+    int tot;
+    const int first = (live && sidx[id] == tid) ? 1 : 0;
+    const int ex = block_exclusive_scan<kSmallRows>(first, sh.wave_sums, &tot);
+    if (first) sidx[id] = ex;
+    if (tid == 0) sh.nseg = tot;
+    lds_sync();
+    build_order1_segments<kSmallRows>(N, cnt, sidx, sst, P, sh);
+  }
+  lds_sync();
+
+  // 3. scatter: live rows at their segment place, the others after all live
+  // rows in batch order
+  const int n_active = sh.nact;
+  const uint64_t dead_mask = __ballot(tid < T && !live);
+  if (lane == 0) sh.wave_dead[wave] = __popcll(dead_mask);
+  lds_sync();
+  if (tid < T) {
+    int pos;
+    if (live) {
+      pos = cnt[id] + __popcll(m & lanemask_lt());
+      for (int w = 0; w < wave; ++w) pos += __popcll(tbl[w * N + id]);
+    } else {
+      pos = n_active + __popcll(dead_mask & lanemask_lt());
+      for (int w = 0; w < wave; ++w) pos += sh.wave_dead[w];
+    }
+    P.perm[pos] = tid;
+    P.pos_seg[pos] = live ? sidx[id] : -1;
+  }
+
+  // 4. summary; R = min{r in {16*2^k < T} U {T} : r >= m_max}
+  if (tid == 0) {
+    const int mmax = sh.mmax;
+    int R = 0;
+    if (n_active > 0) {
+      R = T;
+      for (int r = 16; r < T; r <<= 1)
+        if (r >= mmax) { R = r; break; }
+    }
+    P.sum[kNActive] = n_active;
+    P.sum[kNSegments] = sh.nseg;
+    P.sum[kMMax] = mmax;
+    P.sum[kRowBound] = R;
+    P.sum[kRows] = T;
+    P.sum[kError] = 0;
+    for (int w = 8; w < kSegHeader; ++w) P.sum[w] = 0;
+  }
+}
+
 template <int THREADS>
 hipError_t launch_threads(const int32_t* ids, const uint8_t* active, int T, int n_slots, int order, int32_t* seg,
                           hipStream_t st) {
@@ -377,6 +536,12 @@ hipError_t launch_threads(const int32_t* ids, const uint8_t* active, int T, int 
 
 hipError_t launch_build_segments(const int32_t* ids, const uint8_t* active, int T, int n_slots, int order,
                                  int32_t* seg, hipStream_t st) {
+  if (T <= kSmallRows && n_slots >= 1 && n_slots <= kSmallMaxSlots) {
+    const size_t lds = (size_t)n_slots * (4 * sizeof(uint64_t) + 3 * sizeof(int));
+    hipLaunchKernelGGL(build_segments_small_kernel, dim3(1), dim3(kSmallRows), lds, st, ids, active, T, n_slots,
+                       order, seg);
+    return hipGetLastError();
+  }
   if (T <= 256) return launch_threads<256>(ids, active, T, n_slots, order, seg, st);
   return launch_threads<1024>(ids, active, T, n_slots, order, seg, st);
 }

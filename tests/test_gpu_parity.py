@@ -93,6 +93,59 @@ def test_segments_bit_exact(name, order, device_build):
     assert s.row_bound == (oracle.row_bound(w.T, ref["m_max"]) if ref["n_active"] else 0)
 
 
+def _check_layout(ids, act, N, order):
+    """Device segment buffer against the oracle's grouping, field by field."""
+    T = len(ids)
+    seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=DEV)
+    agm.build_segments_dev(torch.from_numpy(ids).to(DEV), None if act is None else torch.from_numpy(act).to(DEV),
+                           N, seg, order)
+    torch.cuda.synchronize()
+    s = agm.summary_from_words(seg[:agm.SEG_HEADER].cpu().numpy())
+    w = type("W", (), {})()
+    w.T = T
+    d = split_seg(seg, T)
+    ref = oracle.build_segments(ids, np.ones(T, np.uint8) if act is None else act, order)
+    S = ref["S"]
+    case = (T, N, order, act is None)
+    assert s.error == 0 and s.n_active == ref["n_active"] and s.n_segments == S and s.m_max == ref["m_max"], case
+    assert np.array_equal(d["perm"], ref["perm"]), case
+    assert np.array_equal(d["seg_start"][:S + 1], ref["seg_start"]), case
+    assert np.array_equal(d["seg_adapter"][:S], ref["seg_adapter"]), case
+    want_pos = np.full(w.T, -1)
+    for k in range(S):
+        want_pos[ref["seg_start"][k]:ref["seg_start"][k + 1]] = k
+    assert np.array_equal(d["pos_seg"], want_pos), case
+    for key, tile, n in (("tiles_small", 16, s.n_tiles_small), ("tiles_large", 64, s.n_tiles_large)):
+        want = oracle.row_tiles(ref["seg_start"], tile)
+        assert n == len(want), case
+        assert [(int(b), int(a)) for a, b in d[key][:n]] == [(x[0], x[1]) for x in want], case
+    assert s.row_bound == (oracle.row_bound(w.T, ref["m_max"]) if ref["n_active"] else 0), case
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_device_segments_small_batch_kernel(order):
+    """Batches of at most 256 rows with pools of at most 1024 adapters take the
+    lane-mask builder; the edges of that range and just past it (the general
+    builder) must give the oracle's grouping."""
+    g = np.random.default_rng(9 + order)
+    cases = [
+        (256, 1024, g.integers(-1, 1024, 256), None),               # largest pool of the small builder
+        (256, 1025, g.integers(-1, 1025, 256), None),               # one past: the general builder
+        (256, 64, np.minimum(g.zipf(1.1, 256) - 1, 63), (g.uniform(size=256) > 0.5)),
+        (200, 3, np.full(200, 2), None),                            # one adapter for every row
+        (130, 8, g.integers(-1, 8, 130), np.zeros(130, bool)),      # every row inactive
+        (1, 5, np.array([4]), None),                                # a single row
+        (64, 1, np.full(64, -1), None),                             # no adapter anywhere
+        (255, 1000, np.repeat(g.permutation(1000)[:51], 5), None),  # runs spanning waves
+    ]
+    for T, N, ids, act in cases:
+        ids = np.asarray(ids, np.int32)
+        if act is not None:
+            act = np.asarray(act, np.uint8)
+        _check_layout(ids, act, N, order)
+        _check_layout(ids, np.ones(T, np.uint8), N, order)     # flags given, all set
+
+
 def test_device_segments_large_and_bad_ids():
     g = np.random.default_rng(5)
     for T, N in [(1, 1), (1023, 7), (1025, 8192), (5000, 300), (20000, 1024)]:
