@@ -209,7 +209,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   __shared__ float g_scale[BM];
   __shared__ int s_flag, s_sums[NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // with several row fragments per wave the wave index is read into a scalar
+  // register, so that the adapter phase's per-fragment tests branch on SCC
+  // (measured: faster there, slower for one fragment per wave)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = TM > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int frow = lane & 15, fk = lane >> 4;
 
@@ -558,7 +562,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           if (h >= nhalf) break;
           // the groups of this half step are consecutive, so their rows are
           // one range [r_lo, r_hi); fragments outside it multiply zeros
-          const uint32_t hr = hrange[h];
+          // (wave-uniform: with several fragments per wave kept in a scalar
+          // register, so that the fragment skips below are scalar branches)
+          const uint32_t hr = TM > 1 ? __builtin_amdgcn_readfirstlane(hrange[h]) : hrange[h];
           const int r_lo = (int)(hr & 0xffff), r_hi = (int)(hr >> 16);
           const int kc = 4 * h + fk;            // this lane's packed chunk
           const uint32_t rx = kc < n_chunks ? crec[kc].x : 0u;
