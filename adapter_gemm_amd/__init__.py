@@ -30,6 +30,7 @@ EXPORTED = [
     "lora_fused_linear_slices", "lora_fused_slices_workspace_bytes",
     "lora_registry_create", "lora_registry_destroy", "lora_registry_acquire", "lora_registry_release",
     "lora_registry_lookup", "lora_registry_stats", "lora_pool_install",
+    "lora_device_cu_count", "lora_stream_create_cu_masked", "lora_stream_destroy",
     "lora_quantize_e4m3", "lora_status_string", "lora_last_error",
 ]
 
@@ -89,6 +90,9 @@ def _load():
         "lora_registry_lookup": (I32, [P, ctypes.c_int64, P]),
         "lora_registry_stats": (I32, [P, P]),
         "lora_pool_install": (I32, [P, I32, P, P, I32, ctypes.c_float, P]),
+        "lora_device_cu_count": (I32, [P]),
+        "lora_stream_create_cu_masked": (I32, [P, I32, P]),
+        "lora_stream_destroy": (I32, [P]),
         "lora_quantize_e4m3": (I32, [P, I32, I32, I32, P, I32, P, P]),
         "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lora_last_error": (ctypes.c_char_p, []),
@@ -262,6 +266,51 @@ def pool_install(pool: PoolDesc, slot: int, A, B, rank: int, scale: float, strea
     device tensors in the pool dtype), asynchronously on the stream."""
     _check(_lib.lora_pool_install(ctypes.byref(pool), slot, _ptr(A), _ptr(B), rank, scale, _stream(stream)),
            "lora_pool_install")
+
+
+def cu_count() -> int:
+    n = ctypes.c_int32()
+    _check(_lib.lora_device_cu_count(ctypes.byref(n)), "lora_device_cu_count")
+    return int(n.value)
+
+
+def cu_mask_words(cus, n_cus: int):
+    """32-bit mask words with the bits of the given logical CU indices set."""
+    words = [0] * ((n_cus + 31) // 32)
+    for c in cus:
+        if not 0 <= c < n_cus:
+            raise ValueError(f"CU {c} outside 0..{n_cus - 1}")
+        words[c // 32] |= 1 << (c % 32)
+    return words
+
+
+class CUMaskedStream:
+    """A stream whose kernels run only on the given CUs; `.stream` is a torch
+    stream over it (pass it as `stream=` to the calls or to torch's events)."""
+
+    def __init__(self, cus, n_cus: Optional[int] = None):
+        import torch
+        n = cu_count() if n_cus is None else n_cus
+        words = cu_mask_words(cus, n)
+        arr = (ctypes.c_uint32 * len(words))(*words)
+        h = ctypes.c_void_p()
+        _check(_lib.lora_stream_create_cu_masked(arr, len(words), ctypes.byref(h)), "lora_stream_create_cu_masked")
+        self._h = h
+        self._destroy = _lib.lora_stream_destroy
+        self.cus = sorted(set(cus))
+        self.stream = torch.cuda.ExternalStream(h.value)
+
+    def close(self) -> None:
+        # work still queued on the stream completes before its resources go
+        if self._h is not None and self._h.value:
+            self._destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def fused_slices_workspace(T: int, d_in: int, d_outs, base_dtype: int, flags: int = 0, device="cuda"):

@@ -322,6 +322,36 @@ int lora_pool_install(const lora_pool_t* pool, int32_t slot, const void* A, cons
   return hip_status(lora::launch_pool_install(*pool, slot, A, B, rank, scale, static_cast<hipStream_t>(stream)));
 }
 
+// ---- concurrent base / adapter work on disjoint CU sets ----------------------
+
+int lora_device_cu_count(int32_t* n_cus) {
+  if (!n_cus) return LORA_E_ARG;
+  int dev = 0, n = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e);
+  *n_cus = n;
+  return LORA_OK;
+}
+
+int lora_stream_create_cu_masked(const uint32_t* cu_mask, int32_t n_words, void** stream) {
+  if (!stream || !cu_mask || n_words <= 0) return LORA_E_ARG;
+  *stream = nullptr;
+  bool any = false;
+  for (int32_t i = 0; i < n_words; ++i) any = any || cu_mask[i] != 0;
+  if (!any) return LORA_E_ARG;
+  hipStream_t s = nullptr;
+  const int st = hip_status(hipExtStreamCreateWithCUMask(&s, (uint32_t)n_words, cu_mask));
+  if (st != LORA_OK) return st;
+  *stream = s;
+  return LORA_OK;
+}
+
+int lora_stream_destroy(void* stream) {
+  if (!stream) return LORA_E_ARG;
+  return hip_status(hipStreamDestroy(static_cast<hipStream_t>(stream)));
+}
+
 int lora_quantize_e4m3(const void* x, int32_t T, int32_t d, int32_t ld_x, uint8_t* q, int32_t ld_q, float* s_x,
                        void* stream) {
   if (T < 0 || d < 0 || (T > 0 && (!x || !q || !s_x))) return LORA_E_ARG;

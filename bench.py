@@ -53,6 +53,11 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "workload into profiles/ and exit")
     ap.add_argument("--counter-command", default="", help="the command lines that produced the CSVs")
+    ap.add_argument("--concurrent", type=int, default=0, metavar="BASE_CUS",
+                    help="one-projection workloads: time the unfused design instead, the base product on a "
+                         "stream of BASE_CUS compute units and the adapter term on the others")
+    ap.add_argument("--cu-layout", choices=("spread", "block"), default="spread",
+                    help="base CUs: the same share of every block of 32 logical CUs, or the first BASE_CUS")
     return ap.parse_args()
 
 
@@ -219,6 +224,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     n_proj = len(projs)
+    if args.concurrent:
+        concurrent_line(args, w, insts, n_rot, n_slots)
+        return
 
     n_groups = len(groups)
 
@@ -368,6 +376,112 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def concurrent_line(args, w, insts, n_rot: int, n_slots: int) -> None:
+    """The decode step without fusion, base and adapter work side by side on
+    disjoint CU sets ("From Overloaded to Guaranteed" (HALO) 4: base and LoRA
+    layers on partitioned SMs): the base product alone on one CU-masked
+    stream; the segment builder, the shrink and (after the base product) the
+    expand on the other.  The fused step is timed in the same process for
+    comparison.  One JSON line."""
+    import torch
+    import adapter_gemm_amd as agm
+    if len(w.projections) != 1:
+        sys.exit("--concurrent takes a workload of one projection (decode_bgmv, tiny_sgmv)")
+    n_cus = agm.cu_count()
+    k = args.concurrent
+    # (the runtime refuses some masks, e.g. a single CU or 4 CUs of every 32)
+    blocks = max(1, n_cus // 32)
+    if not 0 < k < n_cus or (args.cu_layout == "spread" and k % blocks):
+        sys.exit(f"--concurrent: 0 < BASE_CUS < {n_cus}" + (f", a multiple of {blocks}" if args.cu_layout == "spread" else ""))
+    if args.cu_layout == "spread":
+        base_cus = [c for c in range(n_cus) if c % 32 < k // blocks]
+    else:
+        base_cus = list(range(k))
+    lora_cus = [c for c in range(n_cus) if c not in set(base_cus)]
+    sA, sB = agm.CUMaskedStream(base_cus, n_cus), agm.CUMaskedStream(lora_cus, n_cus)
+    main = torch.cuda.current_stream()
+    T = w.T
+    evs = [tuple(torch.cuda.Event() for _ in range(3)) for _ in range(n_rot)]
+
+    def step_conc(i):
+        inst, seg, ids_d, act_d, _ = insts[i % n_rot]
+        c = inst[0]
+        e0, e_base, e_lora = evs[i % n_rot]
+        e0.record(main)
+        sA.stream.wait_event(e0)
+        sB.stream.wait_event(e0)
+        agm.fused_linear(c["base"], None, None, c["x"], None, c["y"], workspace=c["wsp"], stream=sA.stream)
+        e_base.record(sA.stream)
+        agm.build_segments_dev(ids_d, act_d, n_slots, seg, stream=sB.stream)
+        agm.shrink(c["pool"], seg, T, None, c["x"], c["v"], launch=agm.LAUNCH_PERSISTENT, stream=sB.stream)
+        sB.stream.wait_event(e_base)
+        agm.expand(c["pool"], seg, T, None, c["v"], c["y"], launch=agm.LAUNCH_PERSISTENT, stream=sB.stream)
+        e_lora.record(sB.stream)
+        main.wait_event(e_lora)
+
+    def step_serial(i):                      # the same four calls, one stream
+        inst, seg, ids_d, act_d, _ = insts[i % n_rot]
+        c = inst[0]
+        agm.fused_linear(c["base"], None, None, c["x"], None, c["y"], workspace=c["wsp"])
+        agm.build_segments_dev(ids_d, act_d, n_slots, seg)
+        agm.shrink(c["pool"], seg, T, None, c["x"], c["v"], launch=agm.LAUNCH_PERSISTENT)
+        agm.expand(c["pool"], seg, T, None, c["v"], c["y"], launch=agm.LAUNCH_PERSISTENT)
+
+    def step_fused(i):
+        inst, seg, ids_d, act_d, _ = insts[i % n_rot]
+        c = inst[0]
+        agm.build_segments_dev(ids_d, act_d, n_slots, seg)
+        agm.shrink(c["pool"], seg, T, None, c["x"], c["v"], launch=agm.LAUNCH_PERSISTENT)
+        agm.fused_linear(c["base"], c["pool"], seg, c["x"], c["v"], c["y"], workspace=c["wsp"])
+
+    # A step here costs more host time (launches, events, waits from Python)
+    # than GPU time, so the main stream is held by a spin kernel while the host
+    # queues every timed step; the GPU then runs them back to back and the
+    # events measure GPU time only (the same for the fused step).
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2.4e9 * 400e-6 * args.steps))     # about 0.4 ms of spinning per step
+        t0.record(main)
+        h0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(i)
+        t1.record(main)
+        host_ms = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps, host_ms / args.steps
+
+    ms_conc, host_conc = timed(step_conc)
+    ms_fused, host_fused = timed(step_fused)
+    ms_serial, _ = timed(step_serial)
+    sA.close()
+    sB.close()
+    # the same two-stream step on streams without CU masks: what the
+    # cross-stream waits cost by themselves
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    sA.stream, sB.stream = sA, sB
+    ms_unmasked, _ = timed(step_conc)
+    print(f"# host ms per step to queue: concurrent {host_conc:.3f}, fused {host_fused:.3f}", file=sys.stderr)
+    out = {
+        "metric": METRIC, "value": round(T / (ms_conc * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_conc, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.projections[0].base_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generators; Llama-shaped; random-init adapters)",
+        "config": {"workload": f"{w.name}: {w.description}",
+                   "design": "concurrent CU-masked streams: base product (lora_fused_linear without a pool) on "
+                             f"{len(base_cus)} CUs; build_segments_dev -> shrink -> [after the base] expand on "
+                             f"{len(lora_cus)} CUs",
+                   "cu_layout": args.cu_layout, "T": T, "rotated_instances": n_rot},
+        "fused_ms_per_step": round(ms_fused, 5),
+        "unfused_one_stream_ms_per_step": round(ms_serial, 5),
+        "two_streams_without_masks_ms_per_step": round(ms_unmasked, 5),
+        "concurrent_over_fused": round(ms_conc / ms_fused, 3),
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -16,7 +16,7 @@
  *
  * The layer is split the way the pages split it ("LoRazor" 3.1.1 Eqs. 1-2;
  * "LoRAForge" 2, Multi-LoRA Serving; "EpiLoRA" 3.1, kernels K1 and K2):
- *   lora_build_segments / _dev   group the live rows by adapter (a1, a2)
+ *   lora_build_segments / _dev   group the live rows by adapter
  *   lora_shrink                  v = A_a x          (rank-r down-projection)
  *   lora_expand                  y += s_a B_a v     (unfused up-projection)
  *   lora_fused_linear            y = W0 x (+ s_a B_a v in the epilogue),
@@ -25,6 +25,12 @@
  *                                (q / k / v, gate / up) in one launch
  *   lora_quantize_e4m3           per-token fp8 activation quantisation used
  *                                by the fp8 W8A8 base product
+ *   lora_registry_* / lora_pool_install
+ *                                which adapter occupies which pool slot, and
+ *                                filling a slot ("LLM-stack book" 7.14.3-4)
+ *   lora_stream_create_cu_masked streams on disjoint CU sets, to run the base
+ *                                product and the adapter term side by side
+ *                                (HALO 4) instead of fused
  *
  * Conventions shared by every call
  * --------------------------------
@@ -340,6 +346,31 @@ int lora_registry_stats(const lora_registry_t* registry, int64_t* out4);
  */
 int lora_pool_install(const lora_pool_t* pool, int32_t slot, const void* A, const void* B, int32_t rank,
                       float scale, void* stream);
+
+/* ---- concurrent base and adapter work ---------------------------------- */
+/*
+ * "From Overloaded to Guaranteed" (HALO), 4.1-4.2 and Fig. 6-7: the base layer
+ * and the LoRA layer of a decode step run at the same time on disjoint sets of
+ * compute units, the split chosen by measuring.  Here a split is two HIP
+ * streams restricted to disjoint CU masks: the base product alone
+ * (lora_fused_linear without a pool) on one, lora_shrink on the other, then
+ * lora_expand adds the adapter term once the base product is in y.  The fused
+ * call does the same work in one launch; these calls exist to measure that
+ * alternative.
+ */
+/* *n_cus = compute units of the current device. */
+int lora_device_cu_count(int32_t* n_cus);
+/* New stream on the current device whose kernels run only on the CUs whose bit
+ * is set: bit (i mod 32) of cu_mask[i / 32] is logical CU i, in the numbering of
+ * the HIP runtime's CU masks; n_words 32-bit words are read.  Default priority.
+ * The caller owns the stream (lora_stream_destroy).  Errors: LORA_E_ARG for a
+ * NULL pointer, n_words <= 0 or an all-zero mask (checked before any HIP call);
+ * LORA_E_HIP if the runtime refuses the mask or has no hardware queue left for
+ * it (each CU-masked stream takes a queue of its own; a one-CU mask has been
+ * refused on MI355X). */
+int lora_stream_create_cu_masked(const uint32_t* cu_mask, int32_t n_words, void** stream);
+/* Destroy a stream made by lora_stream_create_cu_masked.  LORA_E_ARG if NULL. */
+int lora_stream_destroy(void* stream);
 
 /*
  * Per-token activation quantisation for the W8A8 base product ("EpiLoRA" 2

@@ -300,3 +300,20 @@ def test_descriptors_keep_their_tensors_alive():
     del A
     gc.collect()
     assert all(r() is not None for r in refs) and p.A == refs[0]().data_ptr()
+
+
+def test_cu_masked_stream_argument_errors():
+    """Bad arguments are refused before any HIP call (no GPU needed)."""
+    lib = agm.lib()
+    h = ctypes.c_void_p()
+    mask = (ctypes.c_uint32 * 8)(*([0xffffffff] * 8))
+    zero = (ctypes.c_uint32 * 8)()
+    assert lib.lora_stream_create_cu_masked(None, 8, ctypes.byref(h)) == 1
+    assert lib.lora_stream_create_cu_masked(mask, 0, ctypes.byref(h)) == 1
+    assert lib.lora_stream_create_cu_masked(mask, 8, None) == 1
+    assert lib.lora_stream_create_cu_masked(zero, 8, ctypes.byref(h)) == 1     # no CU at all
+    assert lib.lora_stream_destroy(None) == 1
+    assert lib.lora_device_cu_count(None) == 1
+    assert agm.cu_mask_words([0, 31, 32, 255], 256) == [0x80000001, 1, 0, 0, 0, 0, 0, 0x80000000]
+    with pytest.raises(ValueError):
+        agm.cu_mask_words([256], 256)

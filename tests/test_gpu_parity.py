@@ -66,7 +66,7 @@ def _v_ref(dp, w, segd):
     return v_rows[segd["perm"][:n]]
 
 
-# ---- a1: segments ------------------------------------------------------------
+# ---- segments ------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("order", [0, 1])
@@ -166,7 +166,7 @@ def test_device_segments_large_and_bad_ids():
     assert s.error == agm.LORA_E_ID
 
 
-# ---- a3 shrink, a4 expand ----------------------------------------------------------
+# ---- shrink, expand -----------------------------------------------------------------
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_shrink_expand_parity(name):
@@ -237,7 +237,7 @@ def test_expand_leaves_other_rows_bitwise_untouched():
     assert rel_l2(to_f64(y), ref) <= TOL["bf16"]
 
 
-# ---- a5 fused linear ----------------------------------------------------------------
+# ---- fused linear -------------------------------------------------------------------
 
 def _fused(dp, seg, s, w, flags=0, zero_base=False, with_pool=True):
     p = dp.p
@@ -493,6 +493,52 @@ def test_order_and_determinism():
     yc = _fused(dp, seg1, s1, w)
     assert np.array_equal(ya, yb)                    # bitwise reproducible
     assert rel_l2(yc, ya) <= 1e-3                    # segment order does not matter
+
+
+# ---- base and adapter work on disjoint CU sets --------------------------------------
+
+@pytest.mark.parametrize("split", [("spread", 128), ("block", 64)])
+def test_concurrent_cu_masked_streams(split):
+    """The unfused design on CU-masked streams: the base product alone on one
+    stream, builder -> shrink -> (after the base product) expand on another;
+    y matches the oracle."""
+    layout, k = split
+    n = agm.cu_count()
+    if layout == "spread":
+        base_cus = [c for c in range(n) if c % 32 < k // max(1, n // 32)]
+    else:
+        base_cus = list(range(k))
+    lora_cus = [c for c in range(n) if c not in set(base_cus)]
+    sA, sB = agm.CUMaskedStream(base_cus, n), agm.CUMaskedStream(lora_cus, n)
+    assert sA.cus == base_cus and sB.cus == lora_cus
+    w = make_workload("decode_bgmv", **SMALL["decode_bgmv"])
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    ids = torch.from_numpy(w.ids).to(DEV)
+    act = torch.from_numpy(w.active).to(DEV)
+    seg = torch.empty(agm.segment_words(w.T), dtype=torch.int32, device=DEV)
+    v = torch.empty(w.T, p.r_cap, device=DEV)
+    y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(torch.bfloat16)
+    main = torch.cuda.current_stream()
+    e0, e_base, e_lora = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
+    e0.record(main)
+    sA.stream.wait_event(e0)
+    sB.stream.wait_event(e0)
+    agm.fused_linear(dp.base, None, None, dp.x, None, y, stream=sA.stream)
+    e_base.record(sA.stream)
+    agm.build_segments_dev(ids, act, p.n_slots, seg, stream=sB.stream)
+    agm.shrink(dp.pool, seg, w.T, None, dp.x, v, launch=agm.LAUNCH_PERSISTENT, stream=sB.stream)
+    sB.stream.wait_event(e_base)
+    agm.expand(dp.pool, seg, w.T, None, v, y, launch=agm.LAUNCH_PERSISTENT, stream=sB.stream)
+    e_lora.record(sB.stream)
+    main.wait_event(e_lora)
+    torch.cuda.synchronize()
+    sA.close()
+    sB.close()
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    got = to_f64(y)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) <= TOL["bf16"] and row_rel_l2(got, ref) <= TOL["bf16"]
 
 
 # ---- edge cases ------------------------------------------------------------------
