@@ -66,21 +66,55 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
   constexpr int KC = 4 * VEC;               // k per chunk (4 lane groups)
   __shared__ f32x4_t red[kWaves][64];
   const SegPtrs P = seg_ptrs(a.seg, a.T);
-  if (!seg_valid(P, a.T)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int frow = lane & 15, fk = lane >> 4;
   const TI* __restrict__ X = static_cast<const TI*>(a.x);
   const TI* __restrict__ Ab = static_cast<const TI*>(a.A);
+  const bool listed = a.mode == LORA_LAUNCH_EXACT || a.mode == LORA_LAUNCH_PERSISTENT;
+  // The metadata of an item is a chain of dependent loads (tile record ->
+  // segment -> adapter -> rank -> operands); each level is a full memory
+  // latency, so independent loads of a level go out together: the summary
+  // words with the first item's tile record, the segment's end and adapter
+  // with the permutation entries of all 16 rows the tile may hold.
+  // (all five loads before any branch; the tile index is clamped into the
+  // list's T entries, T >= 1 for every launch)
+  const int first_tile = min((int)(blockIdx.x / a.nrb), a.T - 1);
+  int rec_p0 = P.tiles_small[2 * first_tile];
+  int rec_seg = P.tiles_small[2 * first_tile + 1];
+  const int n_tiles = P.sum[kNTilesSmall];
+  const int s_err = P.sum[kError], s_rows = P.sum[kRows];
+  // an invalid buffer has no live rows (a listed tile record is never
+  // negative; testing it here also keeps its load ahead of the branch)
+  const bool bad_rec = listed & (first_tile < n_tiles) & ((rec_p0 | rec_seg) < 0);
+  if ((s_err != 0) | (s_rows != a.T) | bad_rec) return;
   int n_items = a.n_items;
-  if (a.mode == LORA_LAUNCH_PERSISTENT) n_items = device_tile_count<LORA_TILE_SMALL>(P) * a.nrb;
+  if (a.mode == LORA_LAUNCH_PERSISTENT) n_items = n_tiles * a.nrb;
   const int nchunk = (a.d_in + KC - 1) / KC;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int tile_item = item / a.nrb;
     const int rb = item - tile_item * a.nrb;
     TileWork w;
-    if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, a.rtiles, w)) continue;
+    if (listed) {
+      if (tile_item >= n_tiles) continue;   // a host count that disagrees with the device buffer
+      if (item != (int)blockIdx.x) {
+        rec_p0 = P.tiles_small[2 * tile_item];
+        rec_seg = P.tiles_small[2 * tile_item + 1];
+      }
+      w.p0 = rec_p0;
+      w.seg = rec_seg;
+    } else if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, a.rtiles, w)) {
+      continue;
+    }
+    // segment end, adapter and the tile's 16 permutation entries (row frow,
+    // or a later valid row past the tile) as one round of loads
+    const int seg_end = P.seg_start[w.seg + 1];
     const int adapter = P.seg_adapter[w.seg];
+    const int my_perm = P.perm[min(w.p0 + frow, a.T - 1)];
+    // an empty use of all three keeps the compiler from sinking the segment
+    // end and the permutation loads past the rank test below
+    asm volatile("" ::"v"(seg_end), "v"(adapter), "v"(my_perm));
+    w.rows = min(LORA_TILE_SMALL, seg_end - w.p0);
     const int r = a.slot_rank[adapter];
     const int j0 = rb * a.db;
     if (j0 >= r) continue;                      // directions beyond the retained rank
@@ -91,7 +125,8 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     const int nchq = (nchunk * Pw + 15) / 16;                // k chunks per slice
     // slots past the tile's rows / the block's directions repeat a valid one;
     // their products are never stored
-    const TI* xr = X + (size_t)P.perm[w.p0 + min(sl, w.rows - 1)] * a.ld_x + fk * VEC;
+    const int xrow = __shfl(my_perm, (lane & ~15) | min(sl, w.rows - 1), 64);
+    const TI* xr = X + (size_t)xrow * a.ld_x + fk * VEC;
     const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(sl, jn - 1)) * a.d_in + fk * VEC;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
