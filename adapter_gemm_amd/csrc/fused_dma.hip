@@ -260,12 +260,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   }
   const int m0 = tm * BM;
 
+  // The segment buffer's summary words, the permutation entries of the
+  // tile's rows and their segment ids go out as one round of loads (the
+  // entries below T are readable whether or not the buffer proves valid, and
+  // are used only if it does); the first slabs can move one memory latency
+  // after the start instead of after a chain of dependent rounds.
   SegPtrs P;
-  bool has_seg = a.seg != nullptr;
-  if (has_seg) {
+  const bool seg_given = a.seg != nullptr;
+  int s_err = 0, s_rows = 0, s_nact = 0, rowseg_ld = -1;
+  int perm_q[LX];
+#pragma unroll
+  for (int q = 0; q < LX; ++q) perm_q[q] = 0;
+  if (seg_given) {
     P = seg_ptrs(const_cast<int32_t*>(a.seg), a.T);
-    has_seg = seg_valid(P, a.T);
+    s_err = P.sum[kError];
+    s_rows = P.sum[kRows];
+    s_nact = P.sum[kNActive];
+#pragma unroll
+    for (int q = 0; q < LX; ++q) {
+      const int pos = m0 + ((wave * LX + q) * 64 + lane) / 8;
+      perm_q[q] = P.perm[min(pos, a.T - 1)];
+    }
+    if (tid < BM) rowseg_ld = P.pos_seg[min(m0 + tid, a.T - 1)];
+#pragma unroll
+    for (int q = 0; q < LX; ++q) asm volatile("" ::"v"(perm_q[q]));   // keep the round together
+    asm volatile("" ::"v"(rowseg_ld), "s"(s_err), "s"(s_rows), "s"(s_nact));
   }
+  const bool has_seg = seg_given && s_err == 0 && s_rows == a.T;
 
   // ---- base k range of this split ----------------------------------------
   int kbeg = 0, kend = 0;
@@ -280,8 +301,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   const bool do_lora = has_seg && a.B != nullptr && (a.lora_split ? split == a.splits : true);
   int n_active = 0, my_rowseg = -1;
   if (do_lora) {
-    n_active = P.sum[kNActive];
-    if (tid < BM && m0 + tid < n_active) my_rowseg = P.pos_seg[m0 + tid];
+    n_active = s_nact;
+    if (tid < BM && m0 + tid < n_active) my_rowseg = rowseg_ld;
   }
 
   // per-lane DMA source offsets (k-step offsets go into soffset)
@@ -292,7 +313,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     const int row = s >> 3, c = (s & 7) ^ (row & 7);
     const int pos = m0 + row;
     uint32_t o = kOOB;
-    if (pos < a.T) o = (uint32_t)((has_seg ? P.perm[pos] : pos) * a.ld_x * XE + c * 16);
+    if (pos < a.T) o = (uint32_t)((has_seg ? perm_q[q] : pos) * a.ld_x * XE + c * 16);
     xoff[q] = o;
   }
 #pragma unroll
