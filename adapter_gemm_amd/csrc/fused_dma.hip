@@ -587,6 +587,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           // register, so that the fragment skips below are scalar branches)
           const uint32_t hr = TM > 1 ? __builtin_amdgcn_readfirstlane(hrange[h]) : hrange[h];
           const int r_lo = (int)(hr & 0xffff), r_hi = (int)(hr >> 16);
+          // a wave of several fragments none of whose rows the half step's
+          // groups cover has nothing to add: it skips the chunk records and B
+          // fragments as well (one fragment per wave: the test below is the same)
+          if constexpr (TM > 1)
+            if (wm * WM + WM <= r_lo || wm * WM >= r_hi) continue;
           const int kc = 4 * h + fk;            // this lane's packed chunk
           const uint32_t rx = kc < n_chunks ? crec[kc].x : 0u;
           const int g = kc < n_chunks ? (int)(rx & 0xff) : -2;
