@@ -117,7 +117,8 @@ struct FusedPlan {
   int splits;          // k splits per tile (1 = none)
   int lora_split;      // 1: one extra workgroup per tile runs the adapter phase
   size_t part_bytes;   // fp32 partial tiles when splits + lora_split > 1
-  size_t counter_bytes;
+  size_t counter_bytes;  // split hand-off counters, or the persistent launch's claim counters
+  bool persist;        // more tiles than CUs, no split: a workgroup per CU claims tiles
 };
 
 // r_cap: the adapter pool's rank capacity, 0 without a pool

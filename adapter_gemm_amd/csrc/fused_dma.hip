@@ -48,6 +48,8 @@ namespace {
 enum DmaMode { kBF16 = 0, kW8A16 = 1, kW8A8 = 2 };
 constexpr uint32_t kOOB = 0x80000000u;   // offset past every descriptor's range: loads return zeros
 constexpr int kLoraNBMax = 4;            // adapter-phase ring slots (at most)
+constexpr int kPersistMinTiles = 256;    // persistent launches above this many tiles (MI355X CUs)
+constexpr int kPersistCounters = 16;     // per-XCD claim counters (8 used), 64 bytes of workspace
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer, gfx9-family descriptor word 3
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -84,6 +86,7 @@ struct DmaArgs {
   uint32_t x_bytes, w_bytes, v_bytes, b_bytes;   // descriptor ranges (b: the whole B pool)
   int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out;
   int tiles_m, tiles_n, group_m, nk, splits, lora_split;
+  int n_work;             // work items: tiles x (splits + lora_split)
   int n_slices;           // > 1: the per-slice fields above come from sl[]
   SliceArgs sl[kMaxSlices];
 };
@@ -186,7 +189,7 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 c) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN>
+template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN, bool PERSIST>
 __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   constexpr int NW = WGM * WGN, NT = 64 * NW;          // waves (WGM x WGN grid) and threads
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
   __shared__ int g_row0[BM], g_row1[BM], g_rank[BM], t_rowseg[BM];
   __shared__ float g_scale[BM];
-  __shared__ int s_flag, s_sums[NW];
+  __shared__ int s_flag, s_claim, s_sums[NW];
 
   // with several row fragments per wave the wave index is read into a scalar
   // register, so that the adapter phase's per-fragment tests branch on SCC
@@ -217,12 +220,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   const int wm = wave / WGN, wn = wave % WGN;
   const int frow = lane & 15, fk = lane >> 4;
 
-  // ---- work item: (tile, split) ------------------------------------------
+  // ---- work items: (tile, split) -----------------------------------------
+  // Item i of XCD x (x = workgroup index mod 8, the XCD the hardware gives
+  // it) is x * (n / 8) + i, so that consecutive items, which share W0
+  // columns, meet in one L2.  One-shot launches take item blockIdx / 8 of
+  // their XCD.  Persistent launches (more tiles than CUs) run a workgroup per
+  // CU that claims the next item of its XCD from a counter until none is
+  // left: a CU that finishes early takes more items, where the hardware would
+  // otherwise hold a ready CU idle behind a busy one.
   const int S_total = a.splits + a.lora_split;
-  int pid = blockIdx.x;
-  {
-    const int nblk = gridDim.x, full = (nblk / 8) * 8;   // consecutive items share an XCD
-    if (pid < full) pid = (pid & 7) * (full / 8) + (pid >> 3);
+  const int full = (a.n_work / 8) * 8, per_xcd = full / 8, xcd = blockIdx.x & 7;
+  // (persistent) a workgroup claims its next item only once it is free:
+  // claiming earlier would hold an item while the adapter phase, whose
+  // length varies from tile to tile, still runs
+  for (int round = 0;; ++round) {
+  int pid;
+  if constexpr (PERSIST) {
+    if (round > 0) lds_barrier();               // every wave is past the last tile's LDS reads
+    if (tid == 0) s_claim = __hip_atomic_fetch_add(&a.counters[xcd], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    const int k = s_claim;
+    if (k < per_xcd) pid = xcd * per_xcd + k;
+    else if (k == per_xcd && full + xcd < a.n_work) pid = full + xcd;
+    else break;
+  } else {
+    if (round > 0) break;
+    pid = blockIdx.x;
+    if (pid < full) pid = (pid & 7) * per_xcd + (pid >> 3);
   }
   const int tile = pid / S_total, split = pid - tile * S_total;
   int tm, tn;
@@ -681,22 +705,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
       }
     }
   }
+  }  // work items
 }
 
 __global__ void zero_words_kernel(int32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN>
+// CUs of the current device (one persistent workgroup each), 256 if the
+// query fails
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return kPersistMinTiles;
+  return n;
+}
+
+template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN, bool PERSIST = false>
 hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
   const int S_total = a.splits + a.lora_split;
-  if (S_total > 1) {
-    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, a.counters, pl.tiles);
+  if (S_total > 1 || pl.persist) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, a.counters,
+                       pl.persist ? kPersistCounters : pl.tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN>), dim3(pl.tiles * S_total),
-                     dim3(64 * WGM * WGN), 0, st, a);
+  const int grid = PERSIST ? std::min(a.n_work, device_cus()) : a.n_work;
+  hipLaunchKernelGGL((fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN, PERSIST>), dim3(grid), dim3(64 * WGM * WGN), 0,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -708,12 +745,17 @@ hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
   }
   // 8 waves (two per SIMD) hide LDS and barrier latency; the wave grids are
   // the measured best per tile (the 64 x 64 W8A16 slab is too small for 8)
+  // (64- and 128-row tiles: persistent above one tile per CU)
   if constexpr (MODE == kW8A16) {
-    if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4, 2, 4>(a, pl, st);
-    return launch_cfg<64, 64, MODE, 4, 2, 2>(a, pl, st);
+    if (pl.bm == 128)
+      return pl.persist ? launch_cfg<128, 128, MODE, 4, 2, 4, true>(a, pl, st)
+                        : launch_cfg<128, 128, MODE, 4, 2, 4>(a, pl, st);
+    return pl.persist ? launch_cfg<64, 64, MODE, 4, 2, 2, true>(a, pl, st) : launch_cfg<64, 64, MODE, 4, 2, 2>(a, pl, st);
   } else {
-    if (pl.bm == 128) return launch_cfg<128, 128, MODE, 4, 4, 2>(a, pl, st);
-    return launch_cfg<64, 64, MODE, 4, 4, 2>(a, pl, st);
+    if (pl.bm == 128)
+      return pl.persist ? launch_cfg<128, 128, MODE, 4, 4, 2, true>(a, pl, st)
+                        : launch_cfg<128, 128, MODE, 4, 4, 2>(a, pl, st);
+    return pl.persist ? launch_cfg<64, 64, MODE, 4, 4, 2, true>(a, pl, st) : launch_cfg<64, 64, MODE, 4, 4, 2>(a, pl, st);
   }
 }
 
@@ -767,8 +809,12 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   if (pl.tiles < 64) pl.splits = std::max(1, std::min(4, pl.nk / 8));
   pl.lora_split = (pl.splits > 1 && r_cap > 0) ? 1 : 0;
   const int S_total = pl.splits + pl.lora_split;
+  // persistent: 64- and 128-row tiles with more tiles than CUs (measured:
+  // 256-row tiles, of even cost, keep the one-shot grid)
+  pl.persist = S_total == 1 && pl.bm < 256 && pl.tiles > kPersistMinTiles;
   pl.part_bytes = S_total > 1 ? (size_t)pl.tiles * S_total * pl.bm * pl.bn * sizeof(float) : 0;
-  pl.counter_bytes = S_total > 1 ? (size_t)pl.tiles * sizeof(int32_t) : 0;
+  pl.counter_bytes = S_total > 1 ? (size_t)pl.tiles * sizeof(int32_t)
+                                 : (pl.persist ? kPersistCounters * sizeof(int32_t) : 0);
   return pl;
 }
 
@@ -810,6 +856,8 @@ FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int ba
     pl.tiles_n = tn;
     pl.tiles = pl.tiles_m * tn;
     if (pl.splits > 1 || n > kMaxSlices) pl.dma = false;
+    pl.persist = pl.splits == 1 && pl.lora_split == 0 && pl.bm < 256 && pl.tiles > kPersistMinTiles;
+    pl.counter_bytes = pl.persist ? kPersistCounters * sizeof(int32_t) : 0;
   }
   return pl;
 }
@@ -871,6 +919,7 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
   a.nk = pl.nk;
   a.splits = pl.splits;
   a.lora_split = sl[0].pool ? pl.lora_split : 0;
+  a.n_work = pl.tiles * (a.splits + a.lora_split);
   a.n_slices = n > 1 ? n : 1;
   if (n > 1) {
     int tn0 = 0;

@@ -555,9 +555,10 @@ hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_
 
 size_t fused_slices_workspace_bytes(int T, int d_in, const int32_t* d_out, const int32_t* r_cap, int n,
                                     int base_dtype, int flags) {
-  // a merged launch needs the W8A8 codes only; slices launched one by one
-  // use their own plans' workspaces, one after another
-  size_t need = fused_quant_bytes(T, d_in, flags, base_dtype);
+  // a merged launch needs the W8A8 codes and, when persistent, 64 bytes of
+  // claim counters after them; slices launched one by one use their own
+  // plans' workspaces, one after another
+  size_t need = fused_quant_bytes(T, d_in, flags, base_dtype) + 64;
   for (int s = 0; s < n; ++s)
     need = std::max(need, fused_workspace_bytes(T, d_in, d_out[s], base_dtype, flags, r_cap[s]));
   return need;

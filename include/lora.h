@@ -247,9 +247,11 @@ int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
  *   workspace / workspace_bytes: device scratch, 256-byte aligned, of at
  *            least lora_fused_workspace_bytes(T, d_in, d_out, base->dtype,
  *            flags) bytes (NULL and 0 when that is 0).  It holds the W8A8
- *            codes and scales, and for batches whose output has too few
- *            tiles to fill the GPU the partial tiles of a split-k schedule
- *            with one counter per tile; the call leaves the counters at zero.
+ *            codes and scales; for batches whose output has too few tiles
+ *            to fill the GPU, the partial tiles of a split-k schedule with
+ *            one counter per tile; for outputs of more tiles than the GPU
+ *            has CUs, 64 bytes of counters from which one workgroup per CU
+ *            claims tiles.  Counters are cleared on the stream before use.
  *            Calls that share a workspace must be ordered on one stream.
  *            LORA_E_SIZE if it is missing or too small.
  * y must not alias x.  Results do not depend on the schedule's timing: split

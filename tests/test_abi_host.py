@@ -199,8 +199,10 @@ def test_quant_and_dev_builder_validation():
     assert lib.lora_build_segments_dev(FAKE, None, 8, agm.DEV_MAX_SLOTS + 1, 0, FAKE, None) == agm.LORA_E_SIZE
     assert lib.lora_build_segments_dev(FAKE, None, 8, 4, 3, FAKE, None) == agm.LORA_E_ARG
     assert lib.lora_build_segments_dev(None, None, 8, 4, 0, FAKE, None) == agm.LORA_E_ARG
-    # bf16 with enough output tiles: no workspace; fp8 W8A8: codes + scales
-    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 0
+    # bf16 filling the GPU exactly once (256 tiles of 64 x 64): no workspace;
+    # more tiles than CUs: 64 bytes of claim counters; fp8 W8A8: codes + scales
+    assert lib.lora_fused_workspace_bytes(256, 64, 4096, agm.BF16, 0) == 0
+    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 64
     assert lib.lora_fused_workspace_bytes(4, 64, 64, agm.FP8_E4M3, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16
     # a small output (10 tiles of 64 x 64): 2 k splits + 1 adapter split per tile
     assert lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0) == 10 * 3 * 64 * 64 * 4 + 10 * 4
@@ -217,9 +219,10 @@ def test_fused_slices_host_checks():
     lone = max(lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0),
                lib.lora_fused_workspace_bytes(100, 1024, 136, agm.BF16, 0))
     assert lib.lora_fused_slices_workspace_bytes(2, 100, 1024, d, agm.BF16, 0) == lone > 0
-    # a merged launch needs no partial tiles
+    # a merged launch needs no partial tiles, only the claim counters of a
+    # persistent launch (64 bytes)
     big = (ctypes.c_int32 * 3)(4096, 1024, 1024)
-    assert lib.lora_fused_slices_workspace_bytes(3, 2048, 4096, big, agm.BF16, 0) == 0
+    assert lib.lora_fused_slices_workspace_bytes(3, 2048, 4096, big, agm.BF16, 0) == 64
     # errors: no slices; base dtypes that differ
     E_ARG, E_DTYPE = 1, 4
     assert lib.lora_fused_linear_slices(0, None, None, None, 0, None, 0, 0, None, None, None, None, None, 0,
