@@ -390,6 +390,38 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    } else if constexpr (MODE == kW8A16) {
+      // every LDS read of the step (both 32-wide k halves) goes out before
+      // the first MFMA; without the scheduling barrier the compiler reuses
+      // one A-fragment register set and waits for each read in turn
+      bf16x8_t fa[2][TM];
+      uint2 c8[2][TN];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * WM + i * 16 + frow;
+          fa[kk][i] = *reinterpret_cast<const bf16x8_t*>(As + sw128(row, kk * 4 + fk));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = wn * WN + j * 16 + frow;
+          // 8 codes at byte kk * 32 + fk * 8 of the 64-byte row
+          c8[kk][j] = *reinterpret_cast<const uint2*>(Ws + sw64(row, kk * 2 + (fk >> 1)) + (fk & 1) * 8);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t fb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = e4m3x8_to_bf16(c8[kk][j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk][i], fb[j], acc[i][j], 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -402,13 +434,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int row = wn * WN + j * 16 + frow;
-          if constexpr (MODE == kBF16) {
-            fb[j] = *reinterpret_cast<const bf16x8_t*>(Ws + sw128(row, kk * 4 + fk));
-          } else {
-            // 8 codes at byte kk * 32 + fk * 8 of the 64-byte row
-            const uint2 c8 = *reinterpret_cast<const uint2*>(Ws + sw64(row, kk * 2 + (fk >> 1)) + (fk & 1) * 8);
-            fb[j] = e4m3x8_to_bf16(c8);
-          }
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(Ws + sw128(row, kk * 4 + fk));
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
