@@ -41,7 +41,8 @@ SMALL = {
 # split-k with a separate adapter workgroup (few output tiles), 64-, 128- and
 # 256-row tiles, fp8 with and without splits, rank capacity 128 (the widened
 # fp8 mode then takes the general kernel), many adapter groups per tile,
-# ragged T and d_out throughout
+# persistent workgroups claiming tiles (64- and 128-row tiles, more tiles than
+# CUs; bf16 and widened fp8), ragged T and d_out throughout
 PIPE = {
     "decode_split": ("decode_bgmv", dict(T=100, d_in=1024, d_out=264, n_slots=40)),
     "decode_64tile": ("decode_bgmv", dict(T=300, d_in=1024, d_out=1048, n_slots=40)),
@@ -50,6 +51,9 @@ PIPE = {
     "prefill_256x128": ("prefill_sgmv", dict(T=2100, d_in=512, d_out=4104, n_slots=24, n_req=9)),
     "fp8_split": ("fp8_fused", dict(T=200, d_in=1024, d_out=904, n_slots=32, r=64)),
     "fp8_r128": ("fp8_fused", dict(T=130, d_in=512, d_out=392, n_slots=16, r=128)),
+    "decode_persistent": ("decode_bgmv", dict(T=600, d_in=1024, d_out=3000, n_slots=40)),       # 64x64, 470 tiles
+    "prefill_persistent128": ("prefill_sgmv", dict(T=1100, d_in=512, d_out=4104, n_slots=24, n_req=5)),  # 128x128, 297
+    "fp8_persistent": ("fp8_fused", dict(T=520, d_in=512, d_out=4112, n_slots=32, r=64)),        # 64x64 W8A16, 585
     "llama_kv": ("llama_layer", dict(n_slots=96, n_req=3, prefill_len=40, n_decode=70,
                                      shapes=[("k", 1024, 264), ("down", 768, 1032)])),
 }
