@@ -200,9 +200,12 @@ def test_quant_and_dev_builder_validation():
     assert lib.lora_build_segments_dev(FAKE, None, 8, 4, 3, FAKE, None) == agm.LORA_E_ARG
     assert lib.lora_build_segments_dev(None, None, 8, 4, 0, FAKE, None) == agm.LORA_E_ARG
     # bf16 filling the GPU exactly once (256 tiles of 64 x 64): no workspace;
-    # more tiles than CUs: 64 bytes of claim counters; fp8 W8A8: codes + scales
+    # more 128-row tiles than CUs (3 x 96 of 128 x 128): 64 bytes of claim
+    # counters; 256-row tiles (16 x 128 of 256 x 256) stay one-shot;
+    # fp8 W8A8: codes + scales
     assert lib.lora_fused_workspace_bytes(256, 64, 4096, agm.BF16, 0) == 0
-    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 64
+    assert lib.lora_fused_workspace_bytes(384, 64, 12288, agm.BF16, 0) == 64
+    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 0
     assert lib.lora_fused_workspace_bytes(4, 64, 64, agm.FP8_E4M3, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16
     # a small output (10 tiles of 64 x 64): 2 k splits + 1 adapter split per tile
     assert lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0) == 10 * 3 * 64 * 64 * 4 + 10 * 4
