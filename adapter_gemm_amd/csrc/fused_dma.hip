@@ -738,13 +738,22 @@ __global__ void zero_words_kernel(int32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// CUs of the current device (one persistent workgroup each), 256 if the
+// CUs of the current device, 256 if the
 // query fails
 int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n <= 0)
     return kPersistMinTiles;
+  return n;
+}
+
+// Workgroups of a kernel that one CU holds at once (registers and LDS), 1
+// if the query fails.
+template <typename K>
+int resident_per_cu(K kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) return 1;
   return n;
 }
 
@@ -757,9 +766,14 @@ hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int grid = PERSIST ? std::min(a.n_work, device_cus()) : a.n_work;
-  hipLaunchKernelGGL((fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN, PERSIST>), dim3(grid), dim3(64 * WGM * WGN), 0,
-                     st, a);
+  auto kernel = fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN, PERSIST>;
+  int grid = a.n_work;
+  if (PERSIST) {
+    // as many persistent workgroups as the chip holds at once
+    static const int per_cu = resident_per_cu(kernel, 64 * WGM * WGN);
+    grid = std::min(a.n_work, device_cus() * per_cu);
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * WGM * WGN), 0, st, a);
   return hipGetLastError();
 }
 
@@ -770,12 +784,16 @@ hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
     if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3, 4, 2>(a, pl, st);
   }
   // 8 waves (two per SIMD) hide LDS and barrier latency; the wave grids are
-  // the measured best per tile (the 64 x 64 W8A16 slab is too small for 8)
+  // the measured best per tile (the 64 x 64 W8A16 slab is too small for 8).
+  // W8A16 128 x 128 runs 4 waves and a 3-slot ring instead, so that two
+  // workgroups share a CU: their barriers are independent, and one's LDS
+  // reads and code widening overlap the other's MFMAs (measured: fp8
+  // 8192 -> 28672, 512 rows, 500 -> 418 us against one 8-wave workgroup).
   // (64- and 128-row tiles: persistent above one tile per CU)
   if constexpr (MODE == kW8A16) {
     if (pl.bm == 128)
-      return pl.persist ? launch_cfg<128, 128, MODE, 4, 2, 4, true>(a, pl, st)
-                        : launch_cfg<128, 128, MODE, 4, 2, 4>(a, pl, st);
+      return pl.persist ? launch_cfg<128, 128, MODE, 3, 2, 2, true>(a, pl, st)
+                        : launch_cfg<128, 128, MODE, 3, 2, 2>(a, pl, st);
     return pl.persist ? launch_cfg<64, 64, MODE, 4, 2, 2, true>(a, pl, st) : launch_cfg<64, 64, MODE, 4, 2, 2>(a, pl, st);
   } else {
     if (pl.bm == 128)
@@ -817,7 +835,9 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   const Cfg* pick = nullptr;
   for (const Cfg& c : cands) {
     if (c.bm == 256 && w8a16) continue;
-    if (!lora_fits(c.bm, c.bn, w8a16, c.stages, r_cap)) continue;
+    // ring slots as launched (W8A16 128 x 128: 3, two workgroups per CU)
+    const int stages = (w8a16 && c.bm == 128) ? 3 : c.stages;
+    if (!lora_fits(c.bm, c.bn, w8a16, stages, r_cap)) continue;
     const long tiles = (long)((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
     if (tiles >= c.min_tiles) { pick = &c; break; }
   }
