@@ -2,10 +2,14 @@
 // adapter segment ("LoRazor" 3.1.1 Eq. 1; "LoRAForge" 5, rank-aware shrink:
 // directions beyond the adapter's retained rank exit before reading operands).
 //
-// bf16 pools: one work item is (row tile of <= 16 rows of one segment, block
-// of db = 16, 8 or 4 rank directions), computed as a 16 x 16 tile of MFMA
-// v_mfma_f32_16x16x32_bf16 products.  Small batches use narrow blocks, so
-// that enough workgroups share the A rows to keep the chip's CUs streaming.
+// bf16 pools: one work item is (row tile of <= 16 rows of one segment, NB
+// consecutive blocks of db = 16, 8 or 4 rank directions), each block computed
+// as a 16 x 16 tile of MFMA v_mfma_f32_16x16x32_bf16 products that share the
+// item's x fragments.  Small batches use narrow blocks and one block per
+// item, so that enough workgroups share the A rows to keep the chip's CUs
+// streaming; batches with more row tiles than that need take several blocks
+// per item, so that a tile's x rows and its chain of metadata loads serve
+// all of its rank directions (blocks past the adapter's rank do no work).
 // Operand fragments come straight from global memory: lane l reads 16
 // contiguous bytes of a token row and 16 of a direction row, at k offset
 // 8 * (l / 16) inside each 32-wide k chunk, so both operands stream in
@@ -25,6 +29,7 @@
 #include "tiles.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace lora {
 namespace {
@@ -38,7 +43,7 @@ struct ShrinkArgs {
   int32_t* seg;
   float* v;
   int ld_x, r_cap, d_in, T, ld_v;
-  int mode, db, nrb, rtiles, n_items;  // n_items: host item count (EXACT/BUCKETED/FULL)
+  int mode, db, nrb, rtiles, n_items;  // nrb: items per row tile; n_items: host item count (EXACT/BUCKETED/FULL)
 };
 
 constexpr int kUnroll = 8;        // k chunks in flight per wave
@@ -60,10 +65,11 @@ __device__ __forceinline__ f32x4_t mfma_chunk(const u32x4_t& xv, const u32x4_t& 
   }
 }
 
-template <typename TI>
+template <typename TI, int NB>
 __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
   constexpr int VEC = 16 / sizeof(TI);      // elements per 16-byte load
   constexpr int KC = 4 * VEC;               // k per chunk (4 lane groups)
+  constexpr int UNR = kUnroll / NB > 0 ? kUnroll / NB : 1;   // k chunks in flight per wave
   __shared__ f32x4_t red[kWaves][64];
   const SegPtrs P = seg_ptrs(a.seg, a.T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -116,9 +122,10 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     asm volatile("" ::"v"(seg_end), "v"(adapter), "v"(my_perm));
     w.rows = min(LORA_TILE_SMALL, seg_end - w.p0);
     const int r = a.slot_rank[adapter];
-    const int j0 = rb * a.db;
+    const int j0 = rb * NB * a.db;
     if (j0 >= r) continue;                      // directions beyond the retained rank
-    const int jn = min(a.db, r - j0);           // directions of this item
+    const int jn = min(a.db, r - j0);           // directions of the item's first block
+    const int nbl = min(NB, (r - j0 + a.db - 1) / a.db);   // blocks with directions below the rank
     const int span = max(w.rows, jn);
     const int Pw = span <= 4 ? 4 : (span <= 8 ? 8 : 16);   // row slots per k slice
     const int sl = frow % Pw, ks = frow / Pw;                // this lane's slot and k slice
@@ -127,42 +134,57 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     // their products are never stored
     const int xrow = __shfl(my_perm, (lane & ~15) | min(sl, w.rows - 1), 64);
     const TI* xr = X + (size_t)xrow * a.ld_x + fk * VEC;
-    const TI* ar = Ab + ((size_t)adapter * a.r_cap + j0 + min(sl, jn - 1)) * a.d_in + fk * VEC;
-
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = wave; c0 < nchq; c0 += kWaves * kUnroll) {
-      u32x4_t xv[kUnroll], av[kUnroll];
+    const TI* ar[NB];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+    for (int b = 0; b < NB; ++b) {
+      const int jb = min(a.db, r - j0 - b * a.db);   // directions of block b (<= 0: no work)
+      ar[b] = Ab + ((size_t)adapter * a.r_cap + j0 + b * a.db + min(sl, max(jb, 1) - 1)) * a.d_in + fk * VEC;
+    }
+
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = wave; c0 < nchq; c0 += kWaves * UNR) {
+      u32x4_t xv[UNR], av[UNR][NB];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
         const int c = c0 + kWaves * u;
         const int g = ks * nchq + c;            // this lane's chunk
         // d_in % 8 == 0: a lane's group is all in or all out
         const bool in = c < nchq && g * KC + fk * VEC < a.d_in;
         xv[u] = in ? ld128(xr + (size_t)g * KC) : u32x4_t{0, 0, 0, 0};
-        av[u] = in ? ld128(ar + (size_t)g * KC) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) av[u][b] = (in && b < nbl) ? ld128(ar[b] + (size_t)g * KC) : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) acc = mfma_chunk<TI>(xv[u], av[u], acc);
-    }
-    // acc[e] = partial product[row = 4 * (lane / 16) + e][col = lane % 16];
-    // v[s, c] is the sum over slices q of product[s + Pw q][c + Pw q]
-    red[wave][lane] = acc;
-    lds_sync();
-    if (threadIdx.x < 256) {
-      const int t = threadIdx.x;              // one output each, slices and waves summed in order
-      const int row = t >> 4, col = t & 15;
-      float s = 0.f;
-      if (row < Pw && col < Pw) {
-        for (int q = 0; q < 16 / Pw; ++q) {
-          const int i = row + Pw * q, j = col + Pw * q;
-          const int src = (i >> 2) * 16 + j, e = i & 3;
+      for (int u = 0; u < UNR; ++u)
 #pragma unroll
-          for (int wv = 0; wv < kWaves; ++wv) s += red[wv][src][e];
+        for (int b = 0; b < NB; ++b) acc[b] = mfma_chunk<TI>(xv[u], av[u][b], acc[b]);
+    }
+    // acc[b][e] = partial product[row = 4 * (lane / 16) + e][col = lane % 16]
+    // of block b; v[s, c] is the sum over slices q of product[s + Pw q][c + Pw q]
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b >= nbl) break;
+      red[wave][lane] = acc[b];
+      lds_sync();
+      if (threadIdx.x < 256) {
+        const int t = threadIdx.x;              // one output each, slices and waves summed in order
+        const int row = t >> 4, col = t & 15;
+        const int jb = min(a.db, r - j0 - b * a.db);
+        float s = 0.f;
+        if (row < Pw && col < Pw) {
+          for (int q = 0; q < 16 / Pw; ++q) {
+            const int i = row + Pw * q, j = col + Pw * q;
+            const int src = (i >> 2) * 16 + j, e = i & 3;
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) s += red[wv][src][e];
+          }
         }
+        if (row < w.rows && col < jb) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + b * a.db + col] = s;
       }
-      if (row < w.rows && col < jn) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + col] = s;
+      lds_sync();
     }
-    lds_sync();
   }
 }
 
@@ -189,7 +211,16 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   const long bound = (long)T / LORA_TILE_SMALL + std::min(T, pool.n_slots);
   a.db = 16;
   while (a.db > 4 && bound * ((pool.r_cap + a.db - 1) / a.db) < kMinItems) a.db >>= 1;
-  a.nrb = (pool.r_cap + a.db - 1) / a.db;
+  const int nblocks = (pool.r_cap + a.db - 1) / a.db;
+  // blocks per item: one, unless the row tiles are mostly full (at least 8
+  // rows on average by the bound), so that sharing a tile's x rows across
+  // blocks saves real traffic; then as many as still leave about kMinItems
+  // items.  (Batches of one- or two-row tiles keep one block per item: their
+  // bytes are the A rows, which must spread over every CU.)
+  int nb = 1;
+  if ((long)T >= 8 * bound)
+    while (nb < 8 && nb < nblocks && bound * ((nblocks + 2 * nb - 1) / (2 * nb)) >= kMinItems) nb *= 2;
+  a.nrb = (nblocks + nb - 1) / nb;
   // row tiles: the bound for PERSISTENT, else the mode's host count
   const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT ? bound : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
   int grid;
@@ -201,10 +232,19 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
     grid = a.n_items;
   }
   if (grid <= 0 || T == 0) return hipSuccess;
-  if (pool.dtype == LORA_BF16)
-    hipLaunchKernelGGL(shrink_mfma_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(shrink_mfma_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
+  auto go = [&](auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    if (pool.dtype == LORA_BF16)
+      hipLaunchKernelGGL((shrink_mfma_kernel<uint16_t, NB>), dim3(grid), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((shrink_mfma_kernel<float, NB>), dim3(grid), dim3(kThreads), 0, st, a);
+  };
+  switch (nb) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
   return hipGetLastError();
 }
 

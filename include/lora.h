@@ -212,9 +212,11 @@ int lora_build_segments_dev(const int32_t* ids, const uint8_t* active, int32_t T
  *   v      device fp32 [T, ld_v], ld_v >= r_cap
  *   summary  host summary of the segment build, or NULL when `launch` is
  *            LORA_LAUNCH_PERSISTENT or LORA_LAUNCH_FULL_BATCH
- * Work items are (row tile of <= LORA_TILE_SMALL rows of one segment, block
- * of 16 rank directions), each a 16 x 16 MFMA tile with operands streamed
- * from global memory; blocks past the adapter's rank do no work.
+ * Work items are (row tile of <= LORA_TILE_SMALL rows of one segment, one
+ * or more blocks of up to 16 rank directions), each block a 16 x 16 MFMA
+ * tile with operands streamed from global memory; long batches of mostly
+ * full tiles put several blocks in one item so that they share the tile's x
+ * rows; blocks past the adapter's rank do no work.
  * Deterministic: fixed-order reductions, no atomics.
  */
 int lora_shrink(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lora_summary_t* summary,

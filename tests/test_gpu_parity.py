@@ -579,6 +579,37 @@ def test_rank_edge_cases(ranks, r_cap):
     assert rel_l2(to_f64(yz), d_ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,r_cap,ranks", [(2048, 64, [64, 1, 33, 17]), (4096, 64, [64, 40, 3, 16]),
+                                           (4096, 128, [128, 100, 5, 33])])
+def test_shrink_several_rank_blocks_per_item(T, r_cap, ranks):
+    """Long batches over few adapters (mostly full 16-row tiles): each shrink
+    item takes 2, 4 or 8 rank blocks that share the tile's x rows.  v matches
+    the oracle on every rank (padding is NaN in the pool) and is bitwise the
+    same in every launch mode."""
+    g = np.random.default_rng(T + r_cap)
+    ids = g.integers(-1, 4, T)
+    w = _custom(T, 264, 200, 4, r_cap, ranks, ids)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, 4)
+    segd = split_seg(seg, T)
+    n = s.n_active
+    vr = _v_ref(dp, w, segd)
+    mask = np.arange(r_cap)[None, :] < p.slot_rank[w.ids[segd["perm"][:n]]][:, None]
+    outs = []
+    for mode in (agm.LAUNCH_EXACT, agm.LAUNCH_PERSISTENT, agm.LAUNCH_BUCKETED, agm.LAUNCH_FULL_BATCH):
+        v = torch.full((T, r_cap), float("nan"), device=DEV)
+        agm.shrink(dp.pool, seg, T, s, dp.x, v, launch=mode)
+        torch.cuda.synchronize()
+        vg = v.cpu().numpy().astype(np.float64)[:n]
+        assert np.isfinite(vg[mask]).all(), mode
+        got = np.where(mask, vg, 0.0)
+        assert rel_l2(got, vr) <= TOL["fp32"] and row_rel_l2(got, vr) <= TOL["fp32"], mode
+        outs.append(vg[mask])
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 @pytest.mark.parametrize("case", ["empty", "all_none", "all_inactive", "one_row", "one_adapter_big"])
 def test_degenerate_batches(case):
     T = {"empty": 0, "one_row": 1}.get(case, 130)
