@@ -832,14 +832,24 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   // (256 x 256 needs two full rounds of the chip to beat 256 x 128's balance)
   struct Cfg { int bm, bn, stages, min_tiles; };
   const Cfg cands[] = {{256, 256, 2, 512}, {256, 128, 3, 256}, {128, 128, 4, 256}, {64, 64, 4, 0}};
+  auto tiles_of = [&](const Cfg& c) { return (long)((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn); };
   const Cfg* pick = nullptr;
   for (const Cfg& c : cands) {
     if (c.bm == 256 && w8a16) continue;
     // ring slots as launched (W8A16 128 x 128: 3, two workgroups per CU)
     const int stages = (w8a16 && c.bm == 128) ? 3 : c.stages;
     if (!lora_fits(c.bm, c.bn, w8a16, stages, r_cap)) continue;
-    const long tiles = (long)((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
-    if (tiles >= c.min_tiles) { pick = &c; break; }
+    if (tiles_of(c) >= c.min_tiles) { pick = &c; break; }
+  }
+  // 256 x 128 against 256 x 256 when the output fills the chip with the
+  // smaller tile: by rounds of one-shot tiles over the CUs, times the
+  // measured cost of one tile (bf16, 4096-deep: 256 x 256 ~114 us, 256 x 128
+  // ~72 us on MI355X), so that 1.5 rounds of the smaller tile do not beat a
+  // part-filled round of the larger one
+  if (pick && pick->bm == 256 && pick->bn == 128 && lora_fits(256, 256, w8a16, cands[0].stages, r_cap)) {
+    const long cus = device_cus();
+    const long r256 = (tiles_of(cands[0]) + cus - 1) / cus, r128 = (tiles_of(*pick) + cus - 1) / cus;
+    if (r256 * 114 < r128 * 72) pick = &cands[0];
   }
   if (!pick) return pl;
   pl.dma = true;

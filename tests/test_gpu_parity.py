@@ -48,7 +48,8 @@ PIPE = {
     "decode_64tile": ("decode_bgmv", dict(T=300, d_in=1024, d_out=1048, n_slots=40)),
     "decode_many_groups": ("decode_bgmv", dict(T=250, d_in=2048, d_out=520, n_slots=200)),
     "prefill_256x256": ("prefill_sgmv", dict(T=4100, d_in=512, d_out=8200, n_slots=24, n_req=9)),
-    "prefill_256x128": ("prefill_sgmv", dict(T=2100, d_in=512, d_out=4104, n_slots=24, n_req=9)),
+    "prefill_256x128": ("prefill_sgmv", dict(T=2000, d_in=512, d_out=4088, n_slots=24, n_req=9)),
+    "prefill_256x256_part": ("prefill_sgmv", dict(T=2100, d_in=512, d_out=4104, n_slots=24, n_req=9)),
     "fp8_split": ("fp8_fused", dict(T=200, d_in=1024, d_out=904, n_slots=32, r=64)),
     "fp8_r128": ("fp8_fused", dict(T=130, d_in=512, d_out=392, n_slots=16, r=128)),
     "decode_persistent": ("decode_bgmv", dict(T=600, d_in=1024, d_out=3000, n_slots=40)),       # 64x64, 470 tiles
