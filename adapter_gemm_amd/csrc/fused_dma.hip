@@ -482,6 +482,100 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     }
   }
 
+  // ---- adapter phase, per output (decode tiles, ranks <= 16) ------------------
+  // Each lane adds, to every output it holds, s_a sum_j v[row, j] B_a[n, j]
+  // of its row's adapter in fp32 ("LoRAForge" 5, RowExpand: a channel's rank
+  // row read whole, the rank-r dot in registers).  The B rows of all its
+  // outputs go out as one round of loads, where the packed-rank MFMA steps
+  // below would take one barrier-separated step per four groups: a 64-row
+  // decode tile holds up to ~25 adapter groups of rank 16.
+  bool row_epi = false;
+  if constexpr (BM == 64 && MODE == kBF16) {
+    row_epi = do_lora && a.r_cap <= 16;
+    if (row_epi) {
+      const int pe = min(m0 + BM, n_active);
+      if (m0 < pe) {
+        vm_barrier<0>();                        // ring free: every wave is past its last main step
+        // raw fp32 v rows [m0, pe) x r_cap into the ring (rows past pe: zeros)
+        const int rq = a.r_cap / 4;
+        const i32x4_t vrs = rsrc(a.v, a.v_bytes);
+        for (int c0 = wave * 64; c0 < BM * rq; c0 += NT) {
+          const int c = c0 + lane;
+          const int row = c / rq, c4 = c - row * rq;
+          const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
+          dma16(vrs, ring + c0 * 16, o, 0u);
+        }
+        // adapter, rank and scale of every live row of the tile (-1: none)
+        if (tid < BM) {
+          int ad = -1, rk = 0;
+          float sc = 0.f;
+          if (my_rowseg >= 0) {
+            ad = P.seg_adapter[my_rowseg];
+            rk = a.slot_rank[ad];
+            sc = a.slot_scale[ad];
+          }
+          g_row0[tid] = ad;
+          g_rank[tid] = rk;
+          g_scale[tid] = sc;
+        }
+        vm_drain();                             // this wave's v rows have landed
+        lds_barrier();
+        const float* V32 = reinterpret_cast<const float*>(ring);
+        const uint16_t* __restrict__ Bp = static_cast<const uint16_t*>(a.B);
+        // this lane's outputs: rows wm WM + 16 i + orow + e, channels
+        // col_base + 16 j + ocol; B rank rows as two 8-wide chunks
+        u32x4_t bq[TM][4][TN][2];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
+            const int ad = g_row0[r], rk = g_rank[r];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int n = n0 + wn * WN + j * 16 + (lane & 15);
+              const bool ok = ad >= 0 && n < a.d_out;
+              const uint16_t* br = Bp + ((size_t)(ok ? ad : 0) * a.d_out + (ok ? n : 0)) * a.r_cap;
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                bq[i][e][j][h] = (ok && 8 * h < rk) ? ld128(br + 8 * h) : u32x4_t{0, 0, 0, 0};
+            }
+          }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
+            const int rk = g_rank[r];
+            const float sc = g_scale[r];
+            float vv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              // rank padding of v and B is never read into the sum
+              const f32x4_t t = q < rq ? *reinterpret_cast<const f32x4_t*>(V32 + r * a.r_cap + 4 * q)
+                                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) vv[4 * q + u] = t[u];
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              float dot = 0.f;
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const int k0 = 8 * h + 2 * u;
+                  const uint32_t b2 = bq[i][e][j][h][u];
+                  if (k0 < rk) dot = fmaf(vv[k0], bf16lo(b2), dot);
+                  if (k0 + 1 < rk) dot = fmaf(vv[k0 + 1], bf16hi(b2), dot);
+                }
+              if (rk > 0) acc[i][j][e] = fmaf(sc, dot, acc[i][j][e]);
+            }
+          }
+      }
+    }
+  }
+
   // ---- adapter phase -------------------------------------------------------
   // The tile's groups are laid end to end along one packed rank axis: group
   // g occupies chunks [off_g, off_g + ceil(r_g / 8)) of 8 ranks.  Packed
@@ -489,7 +583,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // k / 8 (j its rank index inside the group), else 0; packed B[n, k] is
   // B_g[n, j].  A x B^T over the packed axis is exactly the sum of the
   // groups' s_g v B_g^T, run as dense 64-wide MFMA steps.
-  if (do_lora) {
+  if (do_lora && !row_epi) {
     const int pe = min(m0 + BM, n_active);
     if (m0 < pe) {
       vm_barrier<0>();                          // ring free: every wave is past its last main step
