@@ -211,6 +211,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   __shared__ int g_row0[BM], g_row1[BM], g_rank[BM], t_rowseg[BM];
   __shared__ float g_scale[BM];
   __shared__ int s_flag, s_claim, s_sums[NW];
+  // (decode tiles) fp32 v rows of the tile for the per-output adapter epilogue
+  constexpr bool kRowEpi = BM == 64 && MODE == kBF16;
+  __shared__ __attribute__((aligned(16))) float v_rows[kRowEpi ? BM * 16 : 4];
 
   // with several row fragments per wave the wave index is read into a scalar
   // register, so that the adapter phase's per-fragment tests branch on SCC
@@ -293,6 +296,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   const bool seg_given = a.seg != nullptr;
   int s_err = 0, s_rows = 0, s_nact = 0, rowseg_ld = -1;
   int perm_q[LX];
+  int oseg[kRowEpi ? TM * 4 : 1];             // (decode tiles) segment of each output row of this lane
+#pragma unroll
+  for (int q = 0; q < (kRowEpi ? TM * 4 : 1); ++q) oseg[q] = -1;
 #pragma unroll
   for (int q = 0; q < LX; ++q) perm_q[q] = 0;
   if (seg_given) {
@@ -306,6 +312,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
       perm_q[q] = P.perm[min(pos, a.T - 1)];
     }
     if (tid < BM) rowseg_ld = P.pos_seg[min(m0 + tid, a.T - 1)];
+    if constexpr (kRowEpi) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          oseg[i * 4 + e] = P.pos_seg[min(m0 + wm * WM + i * 16 + (lane >> 4) * 4 + e, a.T - 1)];
+#pragma unroll
+      for (int q = 0; q < TM * 4; ++q) asm volatile("" ::"v"(oseg[q]));
+    }
 #pragma unroll
     for (int q = 0; q < LX; ++q) asm volatile("" ::"v"(perm_q[q]));   // keep the round together
     asm volatile("" ::"v"(rowseg_ld), "s"(s_err), "s"(s_rows), "s"(s_nact));
@@ -327,6 +342,66 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   if (do_lora) {
     n_active = s_nact;
     if (tid < BM && m0 + tid < n_active) my_rowseg = rowseg_ld;
+  }
+
+  // (decode tiles, ranks <= 16) the per-output adapter epilogue's operands go
+  // out now and land while the main loop runs: one more dependent round here
+  // (each output row's adapter), then its rank, scale and the B rank rows of
+  // this lane's outputs, and the tile's fp32 v rows into LDS.  The main
+  // loop's waits count these as older operations, which complete first.
+  bool row_epi = false;
+  int ad_o[kRowEpi ? TM * 4 : 1], rk_o[kRowEpi ? TM * 4 : 1];
+  float sc_o[kRowEpi ? TM * 4 : 1];
+  u32x4_t bq[kRowEpi ? TM * 4 : 1][kRowEpi ? TN : 1][2];
+  if constexpr (kRowEpi) {
+    row_epi = do_lora && a.r_cap <= 16;
+    // every load below is unconditional, from an address clamped into the
+    // pool (adapter 0, channel 0 where there is nothing to read), and what
+    // it returns is masked only where it is used: a load under a branch
+    // would make the compiler wait for it before the branches join
+#pragma unroll
+    for (int q = 0; q < TM * 4; ++q) {
+      const int r = wm * WM + (q >> 2) * 16 + (lane >> 4) * 4 + (q & 3);
+      const bool live = row_epi && m0 + r < n_active && oseg[q] >= 0;
+      const int ad = has_seg ? P.seg_adapter[max(oseg[q], 0)] : 0;
+      ad_o[q] = live ? ad : -1;
+    }
+    // buffer loads: without a pool (row_epi false) the ranges are empty and
+    // every load returns zeros without touching memory
+    const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.slot_rank), 0, row_epi ? 0x7fffffff : 0, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t scr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.slot_scale), 0, row_epi ? 0x7fffffff : 0, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t bqr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.B), 0, row_epi ? (int)a.b_bytes : 0, kBufferWord3);
+#pragma unroll
+    for (int q = 0; q < TM * 4; ++q) {
+      const int ad = max(ad_o[q], 0);
+      rk_o[q] = (int)__builtin_amdgcn_raw_buffer_load_b32(rkr, ad * 4, 0, 0);
+      sc_o[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scr, ad * 4, 0, 0));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 16 + (lane & 15);
+        const uint32_t o = (uint32_t)(((size_t)ad * a.d_out + (n < a.d_out ? n : 0)) * a.r_cap * 2);
+        // (capacity 8: the second chunk reads the next row, or zeros past
+        // the pool, and is never used)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          bq[q][j][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bqr, (int)o, h * 16, 0));
+      }
+    }
+    if (row_epi && m0 < min(m0 + BM, n_active)) {
+      // raw fp32 v rows [m0, min(m0 + BM, n_active)) x r_cap (rows past it: zeros)
+      const int pe = min(m0 + BM, n_active);
+      const int rq = a.r_cap / 4;
+      const i32x4_t vrs = rsrc(a.v, a.v_bytes);
+      for (int c0 = wave * 64; c0 < BM * rq; c0 += NT) {
+        const int c = c0 + lane;
+        const int row = c / rq, c4 = c - row * rq;
+        const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
+        dma16(vrs, reinterpret_cast<uint8_t*>(v_rows) + c0 * 16, o, 0u);
+      }
+    }
   }
 
   // per-lane DMA source offsets (k-step offsets go into soffset)
@@ -485,94 +560,45 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // ---- adapter phase, per output (decode tiles, ranks <= 16) ------------------
   // Each lane adds, to every output it holds, s_a sum_j v[row, j] B_a[n, j]
   // of its row's adapter in fp32 ("LoRAForge" 5, RowExpand: a channel's rank
-  // row read whole, the rank-r dot in registers).  The B rows of all its
-  // outputs go out as one round of loads, where the packed-rank MFMA steps
-  // below would take one barrier-separated step per four groups: a 64-row
-  // decode tile holds up to ~25 adapter groups of rank 16.
-  bool row_epi = false;
-  if constexpr (BM == 64 && MODE == kBF16) {
-    row_epi = do_lora && a.r_cap <= 16;
-    if (row_epi) {
-      const int pe = min(m0 + BM, n_active);
-      if (m0 < pe) {
-        vm_barrier<0>();                        // ring free: every wave is past its last main step
-        // raw fp32 v rows [m0, pe) x r_cap into the ring (rows past pe: zeros)
-        const int rq = a.r_cap / 4;
-        const i32x4_t vrs = rsrc(a.v, a.v_bytes);
-        for (int c0 = wave * 64; c0 < BM * rq; c0 += NT) {
-          const int c = c0 + lane;
-          const int row = c / rq, c4 = c - row * rq;
-          const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
-          dma16(vrs, ring + c0 * 16, o, 0u);
+  // row read whole, the rank-r dot in registers), from the operands loaded
+  // before the main loop; the packed-rank MFMA steps below would take one
+  // barrier-separated step per four adapter groups, and a 64-row decode tile
+  // holds up to ~25 groups of rank 16.
+  if constexpr (kRowEpi) {
+    if (row_epi && m0 < min(m0 + BM, n_active)) {
+      vm_barrier<0>();                          // every wave's v rows and B rows have landed
+      const int rq = a.r_cap / 4;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = i * 4 + e;
+          const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
+          const int rk = ad_o[q] >= 0 ? rk_o[q] : 0;    // rows without a live adapter add nothing
+          float vv[16];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // rank padding of v and B is never read into the sum
+            const f32x4_t t = c < rq ? *reinterpret_cast<const f32x4_t*>(v_rows + r * a.r_cap + 4 * c)
+                                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) vv[4 * c + u] = t[u];
+          }
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int k0 = 8 * h + 2 * u;
+                const uint32_t b2 = bq[q][j][h][u];
+                if (k0 < rk) dot = fmaf(vv[k0], bf16lo(b2), dot);
+                if (k0 + 1 < rk) dot = fmaf(vv[k0 + 1], bf16hi(b2), dot);
+              }
+            if (rk > 0) acc[i][j][e] = fmaf(sc_o[q], dot, acc[i][j][e]);
+          }
         }
-        // adapter, rank and scale of every live row of the tile (-1: none)
-        if (tid < BM) {
-          int ad = -1, rk = 0;
-          float sc = 0.f;
-          if (my_rowseg >= 0) {
-            ad = P.seg_adapter[my_rowseg];
-            rk = a.slot_rank[ad];
-            sc = a.slot_scale[ad];
-          }
-          g_row0[tid] = ad;
-          g_rank[tid] = rk;
-          g_scale[tid] = sc;
-        }
-        vm_drain();                             // this wave's v rows have landed
-        lds_barrier();
-        const float* V32 = reinterpret_cast<const float*>(ring);
-        const uint16_t* __restrict__ Bp = static_cast<const uint16_t*>(a.B);
-        // this lane's outputs: rows wm WM + 16 i + orow + e, channels
-        // col_base + 16 j + ocol; B rank rows as two 8-wide chunks
-        u32x4_t bq[TM][4][TN][2];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
-            const int ad = g_row0[r], rk = g_rank[r];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const int n = n0 + wn * WN + j * 16 + (lane & 15);
-              const bool ok = ad >= 0 && n < a.d_out;
-              const uint16_t* br = Bp + ((size_t)(ok ? ad : 0) * a.d_out + (ok ? n : 0)) * a.r_cap;
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-                bq[i][e][j][h] = (ok && 8 * h < rk) ? ld128(br + 8 * h) : u32x4_t{0, 0, 0, 0};
-            }
-          }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
-            const int rk = g_rank[r];
-            const float sc = g_scale[r];
-            float vv[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              // rank padding of v and B is never read into the sum
-              const f32x4_t t = q < rq ? *reinterpret_cast<const f32x4_t*>(V32 + r * a.r_cap + 4 * q)
-                                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int u = 0; u < 4; ++u) vv[4 * q + u] = t[u];
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              float dot = 0.f;
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                  const int k0 = 8 * h + 2 * u;
-                  const uint32_t b2 = bq[i][e][j][h][u];
-                  if (k0 < rk) dot = fmaf(vv[k0], bf16lo(b2), dot);
-                  if (k0 + 1 < rk) dot = fmaf(vv[k0 + 1], bf16hi(b2), dot);
-                }
-              if (rk > 0) acc[i][j][e] = fmaf(sc, dot, acc[i][j][e]);
-            }
-          }
-      }
     }
   }
 
