@@ -580,6 +580,32 @@ def test_rank_edge_cases(ranks, r_cap):
     assert rel_l2(to_f64(yz), d_ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("r_cap,ranks", [(16, [16, 9, 8, 1, 5, 12]), (8, [8, 1, 3, 7, 2, 5])])
+def test_decode_tile_epilogue_ranks(r_cap, ranks):
+    """64 x 64 bf16 tiles with rank capacity <= 16 take the per-output adapter
+    epilogue: ranks below the capacity (a partly used second 8-rank chunk,
+    rank 1, capacity 8 with no second chunk), NaN rank padding, a ragged last
+    column tile, rows with id -1 and released rows."""
+    g = np.random.default_rng(r_cap)
+    T, N = 150, len(ranks)
+    ids = g.integers(-1, N, T)
+    act = (g.random(T) > 0.2).astype(np.uint8)
+    w = _custom(T, 512, 328, N, r_cap, ranks, ids, act)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, N)
+    y = _fused(dp, seg, s, w)
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    assert np.isfinite(y).all()
+    assert rel_l2(y, ref) <= TOL["bf16"] and row_rel_l2(y, ref) <= TOL["bf16"]
+    d = _fused(dp, seg, s, w, zero_base=True)
+    d_ref = oracle.lora_delta(*dp.oracle_args(w))
+    live = oracle.live_rows(w.ids, w.active)
+    assert rel_l2(d, d_ref) <= TOL["bf16"] and row_rel_l2(d[live], d_ref[live]) <= TOL["bf16"]
+    yb = _fused(dp, seg, s, w, with_pool=False)
+    assert np.array_equal(y[~live], yb[~live])
+
+
 @pytest.mark.parametrize("T,r_cap,ranks", [(2048, 64, [64, 1, 33, 17]), (4096, 64, [64, 40, 3, 16]),
                                            (4096, 128, [128, 100, 5, 33])])
 def test_shrink_several_rank_blocks_per_item(T, r_cap, ranks):
