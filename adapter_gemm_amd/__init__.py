@@ -26,7 +26,7 @@ SEG_HEADER = 16
 
 EXPORTED = [
     "lora_segment_words", "lora_build_segments", "lora_plan_segments", "lora_build_segments_dev",
-    "lora_shrink", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
+    "lora_shrink", "lora_build_shrink_dev", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
     "lora_fused_linear_slices", "lora_fused_slices_workspace_bytes",
     "lora_registry_create", "lora_registry_destroy", "lora_registry_acquire", "lora_registry_release",
     "lora_registry_lookup", "lora_registry_stats", "lora_pool_install",
@@ -78,6 +78,7 @@ def _load():
         "lora_build_segments": (I32, [P, P, I32, I32, I32, P, P, P, P]),
         "lora_build_segments_dev": (I32, [P, P, I32, I32, I32, P, P]),
         "lora_shrink": (I32, [P, P, I32, P, P, I32, P, I32, I32, P]),
+        "lora_build_shrink_dev": (I32, [P, P, I32, I32, P, P, P, I32, P, I32, P]),
         "lora_expand": (I32, [P, P, I32, P, P, I32, P, I32, I32, I32, P]),
         "lora_fused_linear": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P, SZ, P]),
         "lora_fused_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
@@ -193,6 +194,14 @@ def shrink(pool: PoolDesc, seg, T: int, summary: Optional[Summary], x, v, launch
     _check(_lib.lora_shrink(ctypes.byref(pool), seg.data_ptr(), T,
                             None if summary is None else ctypes.byref(summary), x.data_ptr(), _ld(x),
                             v.data_ptr(), _ld(v), launch, _stream(stream)), "lora_shrink")
+
+
+def build_shrink_dev(ids, active, pool: PoolDesc, seg, x, v, order: int = 0, stream=None) -> None:
+    """Device segment build and persistent shrink of one batch (one launch for small batches)."""
+    T = int(ids.shape[0])
+    _check(_lib.lora_build_shrink_dev(_ptr(ids), _ptr(active), T, order, ctypes.byref(pool), seg.data_ptr(),
+                                      x.data_ptr(), _ld(x), v.data_ptr(), _ld(v), _stream(stream)),
+           "lora_build_shrink_dev")
 
 
 def expand(pool: PoolDesc, seg, T: int, summary: Optional[Summary], v, y, launch: int = LAUNCH_EXACT,

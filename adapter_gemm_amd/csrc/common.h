@@ -102,6 +102,11 @@ hipError_t launch_build_segments(const int32_t* ids, const uint8_t* active, int 
 hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const LaunchShape& ls,
                          const void* x, int ld_x, float* v, int ld_v, hipStream_t st);
 
+// segment build and persistent shrink in one launch (small batches only)
+bool build_shrink_fits(int T, int n_slots);
+hipError_t launch_build_shrink(const int32_t* ids, const uint8_t* active, int T, int order, const lora_pool_t& pool,
+                               int32_t* seg, const void* x, int ld_x, float* v, int ld_v, hipStream_t st);
+
 hipError_t launch_expand(const lora_pool_t& pool, int32_t* seg, int T, const LaunchShape& ls,
                          const float* v, int ld_v, void* y, int y_dtype, int ld_y, hipStream_t st);
 

@@ -193,6 +193,26 @@ int lora_shrink(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
                                         static_cast<hipStream_t>(stream)));
 }
 
+int lora_build_shrink_dev(const int32_t* ids, const uint8_t* active, int32_t T, int32_t order,
+                          const lora_pool_t* pool, int32_t* seg, const void* x, int32_t ld_x, float* v, int32_t ld_v,
+                          void* stream) {
+  int st = check_pool(pool);
+  if (st != LORA_OK) return st;
+  if (T < 0 || !seg || (T > 0 && (!ids || !x || !v)) || (order != 0 && order != 1)) return LORA_E_ARG;
+  if (pool->n_slots > LORA_DEV_MAX_SLOTS) return LORA_E_SIZE;
+  if (ld_x < pool->d_in || ld_v < pool->r_cap) return LORA_E_ARG;
+  if (ld_x % 8 || ld_v % 4 || !aligned16(x) || !aligned16(v)) return LORA_E_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lora::build_shrink_fits(T, pool->n_slots))
+    return hip_status(lora::launch_build_shrink(ids, active, T, order, *pool, seg, x, ld_x, v, ld_v, s));
+  st = hip_status(lora::launch_build_segments(ids, active, T, pool->n_slots, order, seg, s));
+  if (st != LORA_OK || T == 0) return st;
+  lora::LaunchShape ls;
+  st = launch_shape(LORA_LAUNCH_PERSISTENT, nullptr, T, pool->n_slots, ls);
+  if (st != LORA_OK) return st;
+  return hip_status(lora::launch_shrink(*pool, seg, T, ls, x, ld_x, v, ld_v, s));
+}
+
 int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lora_summary_t* summary,
                 const float* v, int32_t ld_v, void* y, int32_t y_dtype, int32_t ld_y, int32_t launch, void* stream) {
   int st = check_pool(pool);

@@ -25,7 +25,7 @@
 //
 // fp32 pools use the same tiling with v_mfma_f32_16x16x4f32 (four MFMAs per
 // 16-byte load, one per element).
-#include "common.h"
+#include "build_small.h"
 #include "tiles.h"
 
 #include <algorithm>
@@ -65,13 +65,14 @@ __device__ __forceinline__ f32x4_t mfma_chunk(const u32x4_t& xv, const u32x4_t& 
   }
 }
 
-template <typename TI, int NB>
-__global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
+// The shrink items of a launch, by a workgroup of WAVES waves, from the
+// segment buffer P (global memory, or the workgroup's own LDS copy); red is
+// LDS of WAVES x 64 x 16 bytes.
+template <typename TI, int NB, int WAVES>
+__device__ __forceinline__ void shrink_items(const ShrinkArgs& a, const SegPtrs& P, f32x4_t (*red)[64]) {
   constexpr int VEC = 16 / sizeof(TI);      // elements per 16-byte load
   constexpr int KC = 4 * VEC;               // k per chunk (4 lane groups)
   constexpr int UNR = kUnroll / NB > 0 ? kUnroll / NB : 1;   // k chunks in flight per wave
-  __shared__ f32x4_t red[kWaves][64];
-  const SegPtrs P = seg_ptrs(a.seg, a.T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int frow = lane & 15, fk = lane >> 4;
   const TI* __restrict__ X = static_cast<const TI*>(a.x);
@@ -144,11 +145,11 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = wave; c0 < nchq; c0 += kWaves * UNR) {
+    for (int c0 = wave; c0 < nchq; c0 += WAVES * UNR) {
       u32x4_t xv[UNR], av[UNR][NB];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int c = c0 + kWaves * u;
+        const int c = c0 + WAVES * u;
         const int g = ks * nchq + c;            // this lane's chunk
         // d_in % 8 == 0: a lane's group is all in or all out
         const bool in = c < nchq && g * KC + fk * VEC < a.d_in;
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
             const int i = row + Pw * q, j = col + Pw * q;
             const int src = (i >> 2) * 16 + j, e = i & 3;
 #pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) s += red[wv][src][e];
+            for (int wv = 0; wv < WAVES; ++wv) s += red[wv][src][e];
           }
         }
         if (row < w.rows && col < jb) a.v[(size_t)(w.p0 + row) * a.ld_v + j0 + b * a.db + col] = s;
@@ -188,21 +189,55 @@ __global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
   }
 }
 
+template <typename TI, int NB>
+__global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
+  __shared__ f32x4_t red[kWaves][64];
+  shrink_items<TI, NB, kWaves>(a, seg_ptrs(a.seg, a.T), red);
+}
+
+// Small batches (T <= 256 rows, pools of at most 1024 slots): the segment
+// build and the shrink in one launch.  Every workgroup groups the batch
+// itself, into its own LDS copy of the segment buffer (a few microseconds of
+// LDS work, no dependent global round trips), and takes its shrink items
+// from that copy; workgroup 0 also writes the copy out as the segment buffer
+// that later launches read.  This removes a launch and, per item, the chain
+// of segment-buffer loads from global memory.  The segment buffer equals the
+// device builder's bit for bit; v equals the persistent shrink's up to fp32
+// rounding (four waves add the k chunks in another fixed order).
+template <typename TI, int NB>
+__global__ __launch_bounds__(kSmallRows) void build_shrink_kernel(const int32_t* __restrict__ ids,
+                                                                  const uint8_t* __restrict__ active, int N,
+                                                                  int order, ShrinkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint64_t tbl[];   // small_build_lds_bytes(N)
+  __shared__ BuildLds sh;
+  __shared__ __attribute__((aligned(16))) int32_t lseg[kSegHeader + 8 * kSmallRows + 1];
+  __shared__ f32x4_t red[kSmallRows / 64][64];
+  const SegPtrs L = seg_ptrs(lseg, a.T);
+  const bool ok = small_build(ids, active, a.T, N, order, L, tbl, sh);
+  lds_sync();
+  if (blockIdx.x == 0) {
+    const int words = (int)seg_words(a.T);
+    for (int i = threadIdx.x; i < words; i += kSmallRows) a.seg[i] = lseg[i];
+  }
+  if (!ok) return;
+  shrink_items<TI, NB, kSmallRows / 64>(a, L, red);
+}
+
 }  // namespace
 
-hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const LaunchShape& ls, const void* x,
-                         int ld_x, float* v, int ld_v, hipStream_t st) {
-  ShrinkArgs a;
-  a.x = x;
+namespace {
+// Item shape of a shrink launch: rank-block width, blocks per item, items per
+// row tile, and the grid (PERSISTENT: the tile bound; else the mode's count).
+struct ShrinkShape {
+  int nb, grid;
+};
+
+ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, ShrinkArgs& a, int max_grid) {
   a.A = pool.A;
   a.slot_rank = pool.slot_rank;
-  a.seg = seg;
-  a.v = v;
-  a.ld_x = ld_x;
   a.r_cap = pool.r_cap;
   a.d_in = pool.d_in;
   a.T = T;
-  a.ld_v = ld_v;
   a.mode = ls.mode;
   a.rtiles = host_row_tiles(ls, T, LORA_TILE_SMALL);
   // The rank-block width (and with it each item's k folding) follows from
@@ -223,28 +258,74 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   a.nrb = (nblocks + nb - 1) / nb;
   // row tiles: the bound for PERSISTENT, else the mode's host count
   const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT ? bound : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
-  int grid;
+  ShrinkShape sh;
+  sh.nb = nb;
   if (ls.mode == LORA_LAUNCH_PERSISTENT) {
     a.n_items = 0;
-    grid = (int)std::min<long>(tiles * a.nrb, 1024);
+    sh.grid = (int)std::min<long>(tiles * a.nrb, max_grid);
   } else {
     a.n_items = (int)(tiles * a.nrb);
-    grid = a.n_items;
+    sh.grid = a.n_items;
   }
-  if (grid <= 0 || T == 0) return hipSuccess;
-  auto go = [&](auto nb_c) {
+  return sh;
+}
+
+template <typename F>
+void with_nb(int nb, F&& f) {
+  switch (nb) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    default: f(std::integral_constant<int, 8>{}); break;
+  }
+}
+}  // namespace
+
+hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const LaunchShape& ls, const void* x,
+                         int ld_x, float* v, int ld_v, hipStream_t st) {
+  ShrinkArgs a;
+  a.x = x;
+  a.seg = seg;
+  a.v = v;
+  a.ld_x = ld_x;
+  a.ld_v = ld_v;
+  const ShrinkShape sh = shrink_shape(pool, T, ls, a, 1024);
+  if (sh.grid <= 0 || T == 0) return hipSuccess;
+  with_nb(sh.nb, [&](auto nb_c) {
     constexpr int NB = decltype(nb_c)::value;
     if (pool.dtype == LORA_BF16)
-      hipLaunchKernelGGL((shrink_mfma_kernel<uint16_t, NB>), dim3(grid), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((shrink_mfma_kernel<uint16_t, NB>), dim3(sh.grid), dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((shrink_mfma_kernel<float, NB>), dim3(grid), dim3(kThreads), 0, st, a);
-  };
-  switch (nb) {
-    case 1: go(std::integral_constant<int, 1>{}); break;
-    case 2: go(std::integral_constant<int, 2>{}); break;
-    case 4: go(std::integral_constant<int, 4>{}); break;
-    default: go(std::integral_constant<int, 8>{}); break;
-  }
+      hipLaunchKernelGGL((shrink_mfma_kernel<float, NB>), dim3(sh.grid), dim3(kThreads), 0, st, a);
+  });
+  return hipGetLastError();
+}
+
+bool build_shrink_fits(int T, int n_slots) { return T >= 1 && T <= kSmallRows && n_slots >= 1 && n_slots <= 1024; }
+
+hipError_t launch_build_shrink(const int32_t* ids, const uint8_t* active, int T, int order, const lora_pool_t& pool,
+                               int32_t* seg, const void* x, int ld_x, float* v, int ld_v, hipStream_t st) {
+  ShrinkArgs a;
+  a.x = x;
+  a.seg = seg;
+  a.v = v;
+  a.ld_x = ld_x;
+  a.ld_v = ld_v;
+  LaunchShape ls{LORA_LAUNCH_PERSISTENT, 0, 0, std::min(T, pool.n_slots)};
+  // every workgroup builds the segments, so the grid is the item bound (at
+  // least one workgroup, which writes the segment buffer)
+  const ShrinkShape sh = shrink_shape(pool, T, ls, a, 1 << 20);
+  const int grid = std::max(sh.grid, 1);
+  const size_t lds = small_build_lds_bytes(pool.n_slots);
+  with_nb(sh.nb, [&](auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    if (pool.dtype == LORA_BF16)
+      hipLaunchKernelGGL((build_shrink_kernel<uint16_t, NB>), dim3(grid), dim3(kSmallRows), lds, st, ids, active,
+                         pool.n_slots, order, a);
+    else
+      hipLaunchKernelGGL((build_shrink_kernel<float, NB>), dim3(grid), dim3(kSmallRows), lds, st, ids, active,
+                         pool.n_slots, order, a);
+  });
   return hipGetLastError();
 }
 

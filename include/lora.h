@@ -223,6 +223,29 @@ int lora_shrink(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
                 const void* x, int32_t ld_x, float* v, int32_t ld_v, int32_t launch, void* stream);
 
 /*
+ * Device segment build followed by the shrink, for one batch: the segment
+ * buffer of lora_build_segments_dev(ids, active, T, pool->n_slots, order,
+ * seg), bit for bit, and the v of lora_shrink(pool, seg, T, NULL, x, ld_x, v,
+ * ld_v, LORA_LAUNCH_PERSISTENT) up to fp32 rounding (the one-launch kernel
+ * adds the k chunks in another fixed order; it is deterministic, and equal
+ * to the two launches for larger batches) ("LLM-stack book" 7.14.2, the sorted
+ * batch and its segment pointers; "LoRazor" 3.1.1 Eq. 1).  Batches of at most
+ * 256 rows over pools of at most 1024 slots run as one launch in which every
+ * workgroup groups the rows into its own LDS copy of the segment buffer and
+ * takes its shrink items from it (workgroup 0 writes the buffer to `seg`);
+ * larger ones run the two launches.
+ *   ids, active, order, seg: as lora_build_segments_dev (device memory)
+ *   pool, x, ld_x, v, ld_v:  as lora_shrink
+ * Errors: LORA_E_ARG, LORA_E_SIZE (n_slots > LORA_DEV_MAX_SLOTS), LORA_E_RANK,
+ * LORA_E_DTYPE, LORA_E_ALIGN, LORA_E_HIP; every check runs before any launch.
+ * An id out of range is reported in the segment buffer's summary, as by the
+ * device builder, and v is then not written.
+ */
+int lora_build_shrink_dev(const int32_t* ids, const uint8_t* active, int32_t T, int32_t order,
+                          const lora_pool_t* pool, int32_t* seg, const void* x, int32_t ld_x, float* v, int32_t ld_v,
+                          void* stream);
+
+/*
  * Expand ("LoRazor" 3.1.1 Eq. 2; "LoRAForge" 5, RowExpand):
  *   y[perm[p], n] += s_a * sum_{j < r_a} v[p, j] * B_a[n, j]   for p < n_active
  * y is updated in place: fp32, or bf16 rounded once (nearest even) from

@@ -156,6 +156,29 @@ def test_shrink_validation():
     assert _shrink(_pool(), launch=agm.LAUNCH_EXACT) == L.LORA_E_ARG    # EXACT needs the host summary
 
 
+def test_build_shrink_validation():
+    """Every argument check of the combined build-and-shrink call runs before
+    any launch (made-up device addresses are never dereferenced)."""
+    L = agm
+
+    def bs(pool=None, ids=FAKE, T=4, order=0, seg=FAKE, x=FAKE, ld_x=64, v=FAKE, ld_v=16):
+        pool = _pool() if pool is None else pool
+        return agm.lib().lora_build_shrink_dev(ids, None, T, order, ctypes.byref(pool), seg, x, ld_x, v, ld_v, None)
+
+    assert agm.lib().lora_build_shrink_dev(FAKE, None, 4, 0, None, FAKE, FAKE, 64, FAKE, 16, None) == L.LORA_E_ARG
+    assert bs(pool=_pool(r_cap=136)) == L.LORA_E_RANK
+    assert bs(pool=_pool(dtype=7)) == L.LORA_E_DTYPE
+    assert bs(pool=_pool(n_slots=L.DEV_MAX_SLOTS + 1)) == L.LORA_E_SIZE
+    assert bs(ids=None) == L.LORA_E_ARG
+    assert bs(seg=None) == L.LORA_E_ARG
+    assert bs(T=-1) == L.LORA_E_ARG
+    assert bs(order=2) == L.LORA_E_ARG
+    assert bs(ld_x=32) == L.LORA_E_ARG
+    assert bs(ld_v=8) == L.LORA_E_ARG
+    assert bs(x=FAKE + 4) == L.LORA_E_ALIGN
+    assert bs(v=FAKE + 8) == L.LORA_E_ALIGN
+
+
 def test_expand_validation():
     lib = agm.lib()
     p = _pool()

@@ -200,6 +200,88 @@ def test_shrink_expand_parity(name):
         assert np.all(d_got[~live] == 0)                 # rows not live untouched
 
 
+def _seg_meaningful(d, words):
+    """the parts of a segment buffer that its summary declares written"""
+    S, nts, ntl = int(words[1]), int(words[4]), int(words[5])
+    return [d["sum"][:8], d["perm"], d["pos_seg"], d["seg_start"][:S + 1], d["seg_adapter"][:S],
+            d["tiles_small"][:nts], d["tiles_large"][:ntl]]
+
+
+BUILD_SHRINK = {
+    # one launch (T <= 256, <= 1024 slots)
+    "decode_200": ("decode_bgmv", dict(T=200, d_in=1024, d_out=264, n_slots=40), 0),
+    "decode_256_order1": ("decode_bgmv", dict(T=256, d_in=512, d_out=264, n_slots=64), 1),
+    "decode_1024_slots": ("decode_bgmv", dict(T=256, d_in=512, d_out=264, n_slots=1024), 0),
+    "tiny_fp32": ("tiny_sgmv", dict(), 0),
+    "fp8_r64": ("fp8_fused", dict(T=130, d_in=1024, d_out=264, n_slots=32, r=64), 0),
+    # two launches (T > 256)
+    "decode_300": ("decode_bgmv", dict(T=300, d_in=1032, d_out=264, n_slots=40), 0),
+}
+
+
+@pytest.mark.parametrize("case", list(BUILD_SHRINK))
+def test_build_shrink_equals_build_then_shrink(case):
+    """lora_build_shrink_dev gives the device builder's segment buffer bit for
+    bit, and the persistent shrink's v up to fp32 rounding (the one-launch
+    kernel's four waves add the k chunks in another order than the shrink's
+    sixteen): within 1e-6 of it, and within the fp32 gate of the oracle."""
+    name, kw, order = BUILD_SHRINK[case]
+    w = make_workload(name, **kw)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    ids = torch.from_numpy(w.ids.astype(np.int32)).to(DEV)
+    act = torch.from_numpy(w.active.astype(np.uint8)).to(DEV)
+    seg_ref = torch.full((agm.segment_words(w.T),), -7, dtype=torch.int32, device=DEV)
+    v_ref = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+    agm.build_segments_dev(ids, act, p.n_slots, seg_ref, order)
+    agm.shrink(dp.pool, seg_ref, w.T, None, dp.x, v_ref, launch=agm.LAUNCH_PERSISTENT)
+    seg = torch.full((agm.segment_words(w.T),), -9, dtype=torch.int32, device=DEV)
+    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+    agm.build_shrink_dev(ids, act, dp.pool, seg, dp.x, v, order=order)
+    torch.cuda.synchronize()
+    d_ref, d = split_seg(seg_ref, w.T), split_seg(seg, w.T)
+    words = d_ref["sum"]
+    assert int(words[7]) == 0 and np.array_equal(d["sum"][:8], words[:8])
+    for a, b in zip(_seg_meaningful(d, words), _seg_meaningful(d_ref, words)):
+        assert np.array_equal(a, b), case
+    n = int(words[0])
+    mask = np.arange(p.r_cap)[None, :] < p.slot_rank[w.ids[d_ref["perm"][:n]]][:, None]
+    vg, vr = v.cpu().numpy()[:n].astype(np.float64), v_ref.cpu().numpy()[:n].astype(np.float64)
+    assert np.isfinite(vg[mask]).all()
+    assert rel_l2(vg[mask], vr[mask]) <= 1e-6, case
+    # deterministic: a second call gives the same bits
+    v2 = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+    agm.build_shrink_dev(ids, act, dp.pool, seg, dp.x, v2, order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(v2.cpu().numpy()[:n][mask], v.cpu().numpy()[:n][mask])
+    # and against the oracle
+    ref = _v_ref(dp, w, d_ref)
+    assert rel_l2(np.where(mask, vg.astype(np.float64), 0.0), ref) <= TOL["fp32"]
+
+
+def test_build_shrink_bad_id_and_empty():
+    """An id out of range is reported in the summary and v is not written; an
+    empty batch writes the summary only."""
+    w = make_workload("decode_bgmv", T=64, d_in=512, d_out=264, n_slots=16)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    bad = w.ids.astype(np.int32).copy()
+    bad[5] = p.n_slots
+    ids = torch.from_numpy(bad).to(DEV)
+    seg = torch.zeros(agm.segment_words(w.T), dtype=torch.int32, device=DEV)
+    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+    agm.build_shrink_dev(ids, None, dp.pool, seg, dp.x, v)
+    torch.cuda.synchronize()
+    words = seg[:agm.SEG_HEADER].cpu().numpy()
+    assert int(words[7]) == agm.LORA_E_ID and int(words[6]) == w.T
+    assert torch.isnan(v).all()
+    seg0 = torch.full((agm.segment_words(0),), -1, dtype=torch.int32, device=DEV)
+    agm.build_shrink_dev(torch.zeros(0, dtype=torch.int32, device=DEV), None, dp.pool, seg0, dp.x, v)
+    torch.cuda.synchronize()
+    w0 = seg0[:agm.SEG_HEADER].cpu().numpy()
+    assert int(w0[0]) == 0 and int(w0[6]) == 0 and int(w0[7]) == 0
+
+
 @pytest.mark.parametrize("launch", [agm.LAUNCH_EXACT, agm.LAUNCH_PERSISTENT, agm.LAUNCH_BUCKETED,
                                     agm.LAUNCH_FULL_BATCH])
 def test_launch_modes_bitwise_identical(launch):
