@@ -212,15 +212,28 @@ __global__ __launch_bounds__(kSmallRows) void build_shrink_kernel(const int32_t*
   __shared__ BuildLds sh;
   __shared__ __attribute__((aligned(16))) int32_t lseg[kSegHeader + 8 * kSmallRows + 1];
   __shared__ f32x4_t red[kSmallRows / 64][64];
+  __shared__ int32_t lrank[1024];
+  // every slot's rank, loaded beside the ids and kept in LDS: the items then
+  // read their rank with no global round trip
+  int rk[1024 / kSmallRows];
+#pragma unroll
+  for (int q = 0; q < 1024 / kSmallRows; ++q) {
+    const int i = q * kSmallRows + (int)threadIdx.x;
+    rk[q] = i < N ? a.slot_rank[i] : 0;
+  }
   const SegPtrs L = seg_ptrs(lseg, a.T);
   const bool ok = small_build(ids, active, a.T, N, order, L, tbl, sh);
+#pragma unroll
+  for (int q = 0; q < 1024 / kSmallRows; ++q) lrank[q * kSmallRows + threadIdx.x] = rk[q];
   lds_sync();
   if (blockIdx.x == 0) {
     const int words = (int)seg_words(a.T);
     for (int i = threadIdx.x; i < words; i += kSmallRows) a.seg[i] = lseg[i];
   }
   if (!ok) return;
-  shrink_items<TI, NB, kSmallRows / 64>(a, L, red);
+  ShrinkArgs b = a;
+  b.slot_rank = lrank;
+  shrink_items<TI, NB, kSmallRows / 64>(b, L, red);
 }
 
 }  // namespace
