@@ -137,8 +137,11 @@ struct FusedSlice {
   int ld_v;
   void* y;
   int ld_y;
-  int d_out;
+  int d_out;                 // output columns of this slice
+  int col0 = 0;              // its first column within the projection (base, y and pool rows)
 };
+// CUs of the current device (256 if the query fails)
+int fused_device_cus();
 // The plan of one launch over n slices (dma false: the slices go one by one).
 FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int base_dtype, int flags);
 hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, int n, const int32_t* seg, int T,

@@ -67,6 +67,7 @@ struct SliceArgs {
   void* y;
   uint32_t w_bytes, b_bytes, v_bytes;
   int ld_w, d_out, r_cap, ld_v, ld_y;
+  int b_ch, b_n0;         // B pool channels per slot, and the slice's first channel in it
   int tn0;                // first column tile of the slice
 };
 
@@ -85,6 +86,7 @@ struct DmaArgs {
   int32_t* counters;
   uint32_t x_bytes, w_bytes, v_bytes, b_bytes;   // descriptor ranges (b: the whole B pool)
   int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out;
+  int b_ch, b_n0;         // B pool channels per slot, and the first channel of these outputs
   int tiles_m, tiles_n, group_m, nk, splits, lora_split;
   int n_work;             // work items: tiles x (splits + lora_split)
   int n_slices;           // > 1: the per-slice fields above come from sl[]
@@ -277,6 +279,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     a.y = q.y;
     a.w_bytes = q.w_bytes;
     a.b_bytes = q.b_bytes;
+    a.b_ch = q.b_ch;
+    a.b_n0 = q.b_n0;
     a.v_bytes = q.v_bytes;
     a.ld_w = q.ld_w;
     a.d_out = q.d_out;
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn * WN + j * 16 + (lane & 15);
-        const uint32_t o = (uint32_t)(((size_t)ad * a.d_out + (n < a.d_out ? n : 0)) * a.r_cap * 2);
+        const uint32_t o = (uint32_t)(((size_t)ad * a.b_ch + a.b_n0 + (n < a.d_out ? n : 0)) * a.r_cap * 2);
         // (capacity 8: the second chunk reads the next row, or zeros past
         // the pool, and is never used)
 #pragma unroll
@@ -668,7 +672,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
         for (int j = 0; j < w8; ++j) {
           const uint32_t lim = (uint32_t)min(8, grk - 8 * j);
           crec[off + j] = make_uint2((uint32_t)tid | ((uint32_t)j << 8) | (lim << 12),
-                                     (uint32_t)((size_t)gad * a.d_out * a.r_cap * 2 + j * 16));
+                                     (uint32_t)(((size_t)gad * a.b_ch + a.b_n0) * a.r_cap * 2 + j * 16));
         }
       }
       vm_drain();                               // the raw v rows have landed
@@ -938,6 +942,8 @@ bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap) {
 }
 }  // namespace
 
+int fused_device_cus() { return device_cus(); }
+
 FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap) {
   FusedPlan pl{};
   pl.dma = false;
@@ -1045,13 +1051,17 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
   const bool w8a8 = base.dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
   const int wel = base.dtype == LORA_BF16 ? 2 : 1;
   auto fill = [&](SliceArgs& q, const FusedSlice& f) {
-    q.W = f.base.W;
-    q.w_scale = f.base.w_scale;
+    // a slice that starts at column col0 of its projection: base rows, scales
+    // and output columns from there, pool rows from channel col0 on
+    q.W = static_cast<const uint8_t*>(f.base.W) + (size_t)f.col0 * f.base.ld_w * wel;
+    q.w_scale = f.base.w_scale ? f.base.w_scale + f.col0 : nullptr;
     q.B = f.pool ? f.pool->B : nullptr;
     q.slot_rank = f.pool ? f.pool->slot_rank : nullptr;
     q.slot_scale = f.pool ? f.pool->slot_scale : nullptr;
     q.v = f.v;
-    q.y = f.y;
+    q.y = static_cast<uint16_t*>(f.y) + f.col0;
+    q.b_ch = f.pool ? f.pool->d_out : 0;
+    q.b_n0 = f.col0;
     q.w_bytes = (uint32_t)((long)f.d_out * f.base.ld_w * wel);
     q.b_bytes = f.pool ? (uint32_t)((long)f.pool->n_slots * f.pool->d_out * f.pool->r_cap * 2) : 0;
     q.v_bytes = f.pool ? (uint32_t)((long)T * f.ld_v * 4) : 0;
@@ -1080,6 +1090,8 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
   a.x_bytes = (uint32_t)((long)T * ld_x * (w8a8 ? 1 : 2));
   a.w_bytes = q0.w_bytes;
   a.b_bytes = q0.b_bytes;
+  a.b_ch = q0.b_ch;
+  a.b_n0 = q0.b_n0;
   a.v_bytes = q0.v_bytes;
   a.r_cap = q0.r_cap;
   a.ld_v = q0.ld_v;

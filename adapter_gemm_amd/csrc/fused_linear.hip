@@ -26,6 +26,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <vector>
 
 namespace lora {
 namespace {
@@ -564,6 +565,51 @@ size_t fused_slices_workspace_bytes(int T, int d_in, const int32_t* d_out, const
   return need;
 }
 
+namespace {
+// A bf16 launch of 256 x 256 one-shot tiles whose last round would fill at
+// most half the CUs: the full rounds keep those tiles and the remaining
+// columns become a second launch, whose planner picks narrower tiles (the
+// Llama gate/up pair, 2048 rows by 28672 columns: 3.5 rounds of 256 x 256
+// become 3 rounds plus one round of 256 x 128).  Slices are cut at a
+// 256-column boundary; a cut slice continues in the second list from column
+// col0.  False when the launch does not qualify.
+bool split_tail_round(const FusedPlan& pl, const FusedSlice* sl, int n, int T, int d_in, int flags,
+                      std::vector<FusedSlice>& first, std::vector<FusedSlice>& rest, FusedPlan& pl_first,
+                      FusedPlan& pl_rest) {
+  if (sl[0].base.dtype != LORA_BF16 || pl.bm != 256 || pl.bn != 256 || pl.persist || pl.splits != 1 ||
+      pl.lora_split != 0)
+    return false;
+  const long cus = fused_device_cus();
+  const long rounds = pl.tiles / cus, rem = pl.tiles % cus;
+  if (rounds < 1 || rem == 0 || 2 * rem > cus || (rounds * cus) % pl.tiles_m != 0) return false;
+  long left = rounds * cus / pl.tiles_m;       // column tiles of the first launch
+  for (int s = 0; s < n; ++s) {
+    const FusedSlice& f = sl[s];
+    const long nt = (f.d_out + 255) / 256;
+    if (left >= nt) {
+      first.push_back(f);
+      left -= nt;
+    } else if (left > 0) {
+      FusedSlice a = f, b = f;
+      a.d_out = (int)(left * 256);
+      b.d_out = f.d_out - a.d_out;
+      b.col0 = f.col0 + a.d_out;
+      first.push_back(a);
+      rest.push_back(b);
+      left = 0;
+    } else {
+      rest.push_back(f);
+    }
+  }
+  if (first.empty() || rest.empty()) return false;
+  pl_first = plan_fused_slices(T, d_in, first.data(), (int)first.size(), LORA_BF16, flags);
+  pl_rest = plan_fused_slices(T, d_in, rest.data(), (int)rest.size(), LORA_BF16, flags);
+  // both must run as merged pipelined launches that need no workspace
+  auto ok = [](const FusedPlan& q) { return q.dma && q.part_bytes == 0 && q.counter_bytes == 0; };
+  return ok(pl_first) && ok(pl_rest);
+}
+}  // namespace
+
 hipError_t launch_fused_slices(const FusedSlice* sl, int n, int32_t* seg, int T, const void* x, int ld_x, int d_in,
                                int flags, void* workspace, hipStream_t st) {
   if (T == 0 || n <= 0) return hipSuccess;
@@ -586,6 +632,22 @@ hipError_t launch_fused_slices(const FusedSlice* sl, int n, int32_t* seg, int T,
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
+  }
+  {
+    std::vector<FusedSlice> first, rest;
+    FusedPlan pf{}, pr{};
+    if (split_tail_round(pl, sl, n, T, d_in, flags, first, rest, pf, pr)) {
+      bool fits = true;
+      for (const FusedSlice& f : first) fits = fits && fused_dma_fits(pf, T, ld_x, f.d_out, f.base.ld_w, bt, flags, f.pool);
+      for (const FusedSlice& f : rest) fits = fits && fused_dma_fits(pr, T, ld_x, f.d_out, f.base.ld_w, bt, flags, f.pool);
+      if (fits) {
+        hipError_t e = launch_fused_dma_slices(pf, first.data(), (int)first.size(), seg, T, x, ld_x, nullptr, d_in,
+                                               flags, workspace, st);
+        if (e != hipSuccess) return e;
+        return launch_fused_dma_slices(pr, rest.data(), (int)rest.size(), seg, T, x, ld_x, nullptr, d_in, flags,
+                                       workspace, st);
+      }
+    }
   }
   const void* xin = x;
   int ld_in = ld_x;

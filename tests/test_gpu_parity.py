@@ -414,6 +414,10 @@ SLICES = {
     "gate_up_256": ("llama_layer", dict(n_slots=96, n_req=7, prefill_len=300, n_decode=4,
                                         shapes=[("gate", 512, 2056), ("up", 512, 2056)])),
     "fp8_two": ("fp8_fused", [904, 520]),
+    # 640 tiles of 256 x 256 on 256 CUs (2.5 rounds): the last half round
+    # runs as a second launch of 256 x 128 tiles over up's last 4080 columns
+    "gate_up_tail_split": ("llama_layer", dict(n_slots=96, n_req=16, prefill_len=96, n_decode=512,
+                                               shapes=[("gate", 128, 10240), ("up", 128, 10224)])),
 }
 
 
