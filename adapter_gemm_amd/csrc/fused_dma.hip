@@ -903,10 +903,10 @@ hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
 
 template <int MODE>
 hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
-  if constexpr (MODE != kW8A16) {
+  if constexpr (MODE == kBF16)
     if (pl.bm == 256 && pl.bn == 256) return launch_cfg<256, 256, MODE, 2, 4, 2>(a, pl, st);
+  if constexpr (MODE != kW8A16)
     if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3, 4, 2>(a, pl, st);
-  }
   // 8 waves (two per SIMD) hide LDS and barrier latency; the wave grids are
   // the measured best per tile (the 64 x 64 W8A16 slab is too small for 8).
   // W8A16 128 x 128 runs 4 waves and a 3-slot ring instead, so that two
@@ -962,6 +962,9 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   const Cfg* pick = nullptr;
   for (const Cfg& c : cands) {
     if (c.bm == 256 && w8a16) continue;
+    // (W8A8 256 x 256 would need more than 256 registers per lane: the 256 x
+    // 128 tile is its largest)
+    if (c.bm == 256 && c.bn == 256 && w8a8) continue;
     // ring slots as launched (W8A16 128 x 128: 3, two workgroups per CU)
     const int stages = (w8a16 && c.bm == 128) ? 3 : c.stages;
     if (!lora_fits(c.bm, c.bn, w8a16, stages, r_cap)) continue;
@@ -972,7 +975,7 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   // measured cost of one tile (bf16, 4096-deep: 256 x 256 ~114 us, 256 x 128
   // ~72 us on MI355X), so that 1.5 rounds of the smaller tile do not beat a
   // part-filled round of the larger one
-  if (pick && pick->bm == 256 && pick->bn == 128 && lora_fits(256, 256, w8a16, cands[0].stages, r_cap)) {
+  if (pick && pick->bm == 256 && pick->bn == 128 && !w8a8 && lora_fits(256, 256, w8a16, cands[0].stages, r_cap)) {
     const long cus = device_cus();
     const long r256 = (tiles_of(cands[0]) + cus - 1) / cus, r128 = (tiles_of(*pick) + cus - 1) / cus;
     if (r256 * 114 < r128 * 72) pick = &cands[0];

@@ -18,6 +18,8 @@
  * "LoRAForge" 2, Multi-LoRA Serving; "EpiLoRA" 3.1, kernels K1 and K2):
  *   lora_build_segments / _dev   group the live rows by adapter
  *   lora_shrink                  v = A_a x          (rank-r down-projection)
+ *   lora_build_shrink_dev        the device grouping and the shrink of one
+ *                                batch, in one launch for small batches
  *   lora_expand                  y += s_a B_a v     (unfused up-projection)
  *   lora_fused_linear            y = W0 x (+ s_a B_a v in the epilogue),
  *                                bf16 / fp32 / fp8-e4m3 base
