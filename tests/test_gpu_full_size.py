@@ -79,10 +79,12 @@ def _check_slices(w, projs, seg, sel, pos_of_row, n_act):
     torch.cuda.empty_cache()
 
 
-def _run_path(w, dp, seg, flags=0):
+def _run_path(w, dp, seg, flags=0, v=None):
+    """shrink (unless v is given) and fused linear of one projection"""
     p = dp.p
-    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
-    agm.shrink(dp.pool, seg, w.T, None, dp.x, v, launch=agm.LAUNCH_PERSISTENT)
+    if v is None:
+        v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+        agm.shrink(dp.pool, seg, w.T, None, dp.x, v, launch=agm.LAUNCH_PERSISTENT)
     y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(dp.ydtype)
     bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p.base_dtype]
     ws = agm.fused_workspace(w.T, p.d_in, p.d_out, bt, flags, device=DEV)
@@ -99,7 +101,16 @@ def test_full_size_bench_path(name):
     act = torch.from_numpy(w.active.astype(np.uint8)).to(DEV)
     N = w.projections[0].n_slots
     seg = torch.empty(agm.segment_words(w.T), dtype=torch.int32, device=DEV)
-    agm.build_segments_dev(ids, act, N, seg)
+    # as bench.py: batches of <= 256 rows build the segments and the first
+    # projection's shrink in one launch
+    combined = w.T <= 256 and N <= 1024
+    dp0 = v0 = None
+    if combined:
+        dp0 = DevProjection(w, w.projections[0])
+        v0 = torch.full((w.T, dp0.p.r_cap), float("nan"), device=DEV)
+        agm.build_shrink_dev(ids, act, dp0.pool, seg, dp0.x, v0)
+    else:
+        agm.build_segments_dev(ids, act, N, seg)
     torch.cuda.synchronize()
     d = split_seg(seg, w.T)
     ref = oracle.build_segments(w.ids, w.active, 0)
@@ -120,8 +131,9 @@ def test_full_size_bench_path(name):
             _check_slices(w, [w.projections[names.index(n)] for n in grp], seg, sel, pos_of_row, n_act)
             continue
         p = w.projections[names.index(grp[0])]
-        dp = DevProjection(w, p)
-        v, y = _run_path(w, dp, seg)
+        first = combined and p is w.projections[0]
+        dp = dp0 if first else DevProjection(w, p)
+        v, y = _run_path(w, dp, seg, v=v0 if first else None)
         args = dp.oracle_args(w)
         xs = dp.x_host[sel]
         ids_s, act_s = w.ids[sel], w.active[sel]
