@@ -142,7 +142,8 @@ def stored_traffic(workload: str):
 def main():
     args = parse()
     if args.counter_summary:
-        summarise_counters(args.counter_summary[0], args.counter_summary[1], args.config,
+        summarise_counters(args.counter_summary[0], args.counter_summary[1],
+                           args.config + ("_w8a8" if args.w8a8 else ""),
                            args.calibrate_copy_mb or 256, args.counter_command)
         return
     if args.gpus != 1:
@@ -358,7 +359,8 @@ def main():
     roof["kernel"] = "fused_f32_kernel" if base == "fp32" else DOMINANT
     roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_groups
     roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_groups
-    roof["traffic"] = stored_traffic(w.name)
+    # (a reading belongs to one kernel: the W8A8 option runs another one)
+    roof["traffic"] = stored_traffic(w.name + ("_w8a8" if args.w8a8 else ""))
 
     value = T / (ms_step * 1e-3)
     out = {
