@@ -42,7 +42,13 @@
  *   state; a registry handle owns only host memory.
  * Streams.  Every call is asynchronous on the given hipStream_t (passed as
  *   void*; NULL = the null stream).  No call synchronises the stream or reads
- *   device memory back to the host.
+ *   device memory back to the host.  The device-side calls
+ *   (lora_build_segments_dev, lora_build_shrink_dev, lora_shrink, lora_expand,
+ *   lora_fused_linear, lora_fused_linear_slices) enqueue kernels only (work
+ *   counters are cleared by a kernel, never by hipMemsetAsync), so a HIP graph
+ *   can capture a step and replay it.  lora_build_segments groups the rows on
+ *   the host when it is called, so a captured copy of it would replay that
+ *   one batch: use the device builder under capture.
  * Errors.  Every call returns an int status (LORA_OK = 0).  All argument
  *   checks run before any work is enqueued; a call that returns an error has
  *   modified no output.  Device-side id validation (lora_build_segments_dev)
