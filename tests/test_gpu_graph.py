@@ -92,3 +92,47 @@ def test_graph_replay_equals_eager(name):
         print(f"[graph] {name}: replay {rep} bit-identical", flush=True)
     del g
     torch.cuda.empty_cache()
+
+
+def test_graph_replay_sliced_launch():
+    """q / k / v of the Llama layer set as one sliced launch on one input,
+    after the device build and one shrink per projection."""
+    w = make_workload("llama_layer")
+    names = [p.name for p in w.projections]
+    dps = [DevProjection(w, w.projections[names.index(n)], nan_fill=False) for n in ("q_proj", "k_proj", "v_proj")]
+    print(f"[graph] llama_layer q/k/v: T={w.T}", flush=True)
+    x = dps[0].x
+    ids = torch.from_numpy(w.ids.astype(np.int32)).to(DEV)
+    act = torch.from_numpy(w.active.astype(np.uint8)).to(DEV)
+    seg = torch.empty(agm.segment_words(w.T), dtype=torch.int32, device=DEV)
+    vs = [torch.empty((w.T, dp.p.r_cap), dtype=torch.float32, device=DEV) for dp in dps]
+    ys = [torch.empty((w.T, dp.p.d_out), dtype=dp.ydtype, device=DEV) for dp in dps]
+    ws = agm.fused_slices_workspace(w.T, dps[0].p.d_in, [dp.p.d_out for dp in dps], agm.BF16, device=DEV)
+
+    def step():
+        agm.build_segments_dev(ids, act, dps[0].p.n_slots, seg)
+        for dp, v in zip(dps, vs):
+            agm.shrink(dp.pool, seg, w.T, None, x, v, launch=agm.LAUNCH_PERSISTENT)
+        agm.fused_linear_slices([dp.base for dp in dps], [dp.pool for dp in dps], seg, x, vs, ys, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    y_ref = [y.view(torch.int16).clone() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = torch.randn(1024, 1024, device=DEV)
+    for rep in range(REPLAYS):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for dp, y, ref in zip(dps, ys, y_ref):
+            assert torch.equal(y.view(torch.int16), ref), (dp.p.name, rep)
+        other = torch.tanh(other @ other.T * 1e-3)
+        torch.cuda.synchronize()
+        print(f"[graph] llama_layer q/k/v: replay {rep} bit-identical", flush=True)
+    del g
+    torch.cuda.empty_cache()
