@@ -27,6 +27,7 @@ SEG_HEADER = 16
 EXPORTED = [
     "lora_segment_words", "lora_build_segments", "lora_plan_segments", "lora_build_segments_dev",
     "lora_shrink", "lora_build_shrink_dev", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
+    "lora_fused_workspace_bytes_rcap",
     "lora_fused_linear_slices", "lora_fused_slices_workspace_bytes",
     "lora_registry_create", "lora_registry_destroy", "lora_registry_acquire", "lora_registry_release",
     "lora_registry_lookup", "lora_registry_stats", "lora_pool_install",
@@ -82,6 +83,7 @@ def _load():
         "lora_expand": (I32, [P, P, I32, P, P, I32, P, I32, I32, I32, P]),
         "lora_fused_linear": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P, SZ, P]),
         "lora_fused_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+        "lora_fused_workspace_bytes_rcap": (SZ, [I32, I32, I32, I32, I32, I32]),
         "lora_fused_linear_slices": (I32, [I32, P, P, P, I32, P, I32, I32, P, P, P, P, P, I32, P, SZ, P]),
         "lora_fused_slices_workspace_bytes": (SZ, [I32, I32, I32, P, I32, I32]),
         "lora_registry_create": (I32, [I32, I32, P]),

@@ -11,6 +11,8 @@
 #include "common.h"
 #include "tiles.h"
 
+#include <algorithm>
+
 namespace lora {
 namespace {
 
@@ -23,10 +25,8 @@ struct ExpandArgs {
   void* y;
   int r_cap, d_out, T, ld_v, ld_y;
   int mode, ncb, rtiles, n_items;
+  int slots;                      // L = min(T, n_slots) adapter slots (BUCKETED)
 };
-
-template <typename TB, typename TY, int NPT>
-__device__ __forceinline__ void load_y(const TY* p, float (&o)[NPT]);
 
 template <typename TY, int NPT>
 __device__ __forceinline__ void ld_vals(const TY* p, float (&o)[NPT]) {
@@ -112,14 +112,22 @@ __global__ __launch_bounds__(THREADS) void expand_kernel(ExpandArgs a) {
   if (!seg_valid(P, a.T)) return;
   const TB* __restrict__ Bp = static_cast<const TB*>(a.B);
   TY* __restrict__ Y = static_cast<TY*>(a.y);
-  int n_items = a.n_items;
-  if (a.mode == LORA_LAUNCH_PERSISTENT) n_items = device_tile_count<LORA_TILE_SMALL>(P) * a.ncb;
+  // The work comes from the device summary in every mode; the host summary
+  // (EXACT, BUCKETED) only sizes the grid, which strides over the items, so
+  // a summary of another batch costs time, never rows.
+  int n_items = a.n_items, rtiles = a.rtiles;
+  if (a.mode == LORA_LAUNCH_PERSISTENT || a.mode == LORA_LAUNCH_EXACT) {
+    n_items = device_tile_count<LORA_TILE_SMALL>(P) * a.ncb;
+  } else if (a.mode == LORA_LAUNCH_BUCKETED) {
+    rtiles = (P.sum[kRowBound] + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
+    n_items = a.slots * rtiles * a.ncb;
+  }
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int tile_item = item / a.ncb;
     const int cb = item - tile_item * a.ncb;
     TileWork w;
-    if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, a.rtiles, w)) continue;
+    if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, rtiles, w)) continue;
     const int adapter = P.seg_adapter[w.seg];
     const int r = a.slot_rank[adapter];
     if (r <= 0) continue;
@@ -173,7 +181,7 @@ hipError_t launch_rc(ExpandArgs a, const LaunchShape& ls, int T, hipStream_t st)
     grid = 2048;
   } else {
     a.n_items = host_tile_items(ls, T, LORA_TILE_SMALL) * a.ncb;
-    grid = a.n_items;
+    grid = std::max(a.n_items, 1);   // (at least one workgroup, which finds the device's own count)
   }
   if (grid <= 0) return hipSuccess;
   if (small)
@@ -212,6 +220,7 @@ hipError_t launch_expand(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   a.ld_v = ld_v;
   a.ld_y = ld_y;
   a.mode = ls.mode;
+  a.slots = ls.slots;
   if (pool.dtype == LORA_BF16) {
     if (y_dtype == LORA_BF16) return launch_typed<uint16_t, uint16_t>(a, ls, T, st);
     return launch_typed<uint16_t, float>(a, ls, T, st);

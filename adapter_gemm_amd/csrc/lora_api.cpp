@@ -232,8 +232,20 @@ int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
 size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags) {
   if (T <= 0 || d_in <= 0 || d_out <= 0) return 0;
   if (base_dtype != LORA_F32 && base_dtype != LORA_BF16 && base_dtype != LORA_FP8_E4M3) return 0;
-  // the smallest rank capacity admits every schedule: its size covers the others
-  return lora::fused_workspace_bytes(T, d_in, d_out, base_dtype, flags, 8);
+  // The schedule depends on the pool's rank capacity (larger capacities leave
+  // less LDS for the larger tiles, whose launches may then need claim
+  // counters), so the size returned covers every capacity, and no pool.
+  size_t need = lora::fused_workspace_bytes(T, d_in, d_out, base_dtype, flags, 0);
+  for (int rc = 4; rc <= LORA_MAX_RANK; rc += 4)
+    need = std::max(need, lora::fused_workspace_bytes(T, d_in, d_out, base_dtype, flags, rc));
+  return need;
+}
+
+size_t lora_fused_workspace_bytes_rcap(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags,
+                                       int32_t r_cap) {
+  if (T <= 0 || d_in <= 0 || d_out <= 0 || r_cap < 0 || r_cap > LORA_MAX_RANK) return 0;
+  if (base_dtype != LORA_F32 && base_dtype != LORA_BF16 && base_dtype != LORA_FP8_E4M3) return 0;
+  return lora::fused_workspace_bytes(T, d_in, d_out, base_dtype, flags, r_cap);
 }
 
 }  // extern "C"
@@ -295,10 +307,16 @@ size_t lora_fused_slices_workspace_bytes(int32_t n_slices, int32_t T, int32_t d_
                                          int32_t base_dtype, int32_t flags) {
   if (n_slices <= 0 || !d_out || T <= 0 || d_in <= 0) return 0;
   if (base_dtype != LORA_F32 && base_dtype != LORA_BF16 && base_dtype != LORA_FP8_E4M3) return 0;
-  std::vector<int32_t> rc(n_slices, 8);   // as lora_fused_workspace_bytes: the smallest rank capacity
   for (int s = 0; s < n_slices; ++s)
     if (d_out[s] < 0) return 0;
-  return lora::fused_slices_workspace_bytes(T, d_in, d_out, rc.data(), n_slices, base_dtype, flags);
+  // as lora_fused_workspace_bytes: the largest size over every rank capacity
+  // (the launch plans with the slices' largest capacity), and no pool
+  size_t need = 0;
+  for (int rc = 0; rc <= LORA_MAX_RANK; rc += 4) {
+    const std::vector<int32_t> rcs(n_slices, rc);
+    need = std::max(need, lora::fused_slices_workspace_bytes(T, d_in, d_out, rcs.data(), n_slices, base_dtype, flags));
+  }
+  return need;
 }
 
 int lora_fused_linear_slices(int32_t n_slices, const lora_base_t* bases, const lora_pool_t* pools,

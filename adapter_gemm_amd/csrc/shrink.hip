@@ -43,7 +43,8 @@ struct ShrinkArgs {
   int32_t* seg;
   float* v;
   int ld_x, r_cap, d_in, T, ld_v;
-  int mode, db, nrb, rtiles, n_items;  // nrb: items per row tile; n_items: host item count (EXACT/BUCKETED/FULL)
+  int mode, db, nrb, rtiles, n_items;  // nrb: items per row tile; n_items: host item count (FULL_BATCH)
+  int slots;                           // L = min(T, n_slots) adapter slots (BUCKETED)
 };
 
 constexpr int kUnroll = 8;        // k chunks in flight per wave
@@ -94,8 +95,16 @@ __device__ __forceinline__ void shrink_items(const ShrinkArgs& a, const SegPtrs&
   // negative; testing it here also keeps its load ahead of the branch)
   const bool bad_rec = listed & (first_tile < n_tiles) & ((rec_p0 | rec_seg) < 0);
   if ((s_err != 0) | (s_rows != a.T) | bad_rec) return;
-  int n_items = a.n_items;
-  if (a.mode == LORA_LAUNCH_PERSISTENT) n_items = n_tiles * a.nrb;
+  // The work comes from the device summary in every mode; the host summary
+  // (EXACT, BUCKETED) only sizes the grid, which strides over the items, so
+  // a summary of another batch costs time, never rows.
+  int n_items = a.n_items, rtiles = a.rtiles;
+  if (listed) {
+    n_items = n_tiles * a.nrb;
+  } else if (a.mode == LORA_LAUNCH_BUCKETED) {
+    rtiles = (P.sum[kRowBound] + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
+    n_items = a.slots * rtiles * a.nrb;
+  }
   const int nchunk = (a.d_in + KC - 1) / KC;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -110,7 +119,7 @@ __device__ __forceinline__ void shrink_items(const ShrinkArgs& a, const SegPtrs&
       }
       w.p0 = rec_p0;
       w.seg = rec_seg;
-    } else if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, a.rtiles, w)) {
+    } else if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, rtiles, w)) {
       continue;
     }
     // segment end, adapter and the tile's 16 permutation entries (row frow,
@@ -253,6 +262,7 @@ ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, 
   a.T = T;
   a.mode = ls.mode;
   a.rtiles = host_row_tiles(ls, T, LORA_TILE_SMALL);
+  a.slots = ls.slots;
   // The rank-block width (and with it each item's k folding) follows from
   // the batch shape alone, through the bound sum_a ceil(m_a / 16) <= T / 16 +
   // min(T, n_slots) of the row tiles, so v is the same in every launch mode.
@@ -278,7 +288,8 @@ ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, 
     sh.grid = (int)std::min<long>(tiles * a.nrb, max_grid);
   } else {
     a.n_items = (int)(tiles * a.nrb);
-    sh.grid = a.n_items;
+    // (at least one workgroup, which finds the device's own count)
+    sh.grid = std::max(a.n_items, 1);
   }
   return sh;
 }

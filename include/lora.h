@@ -99,7 +99,11 @@ enum { LORA_F32 = 0, LORA_BF16 = 1, LORA_FP8_E4M3 = 2 };
 /* ---- launch sizing (LoRazor 3.1) -------------------------------------- */
 enum {
   /* grid = exactly the row tiles that hold live rows (sum_a ceil(m_a/BM))
-     times the column blocks; needs the host summary.                      */
+     times the column blocks; needs the host summary.  In EXACT and
+     BUCKETED the host summary sizes the grid only: the kernels take the
+     work itself from the device segment buffer and stride over it, so a
+     summary that does not match the buffer (another batch of the same T)
+     costs time, never rows.                                               */
   LORA_LAUNCH_EXACT = 0,
   /* fixed grid that strides over the device-side tile count; needs no host
      summary, so the launch shape does not change from batch to batch.    */
@@ -169,6 +173,11 @@ typedef struct {
  *   tiles_small [2T]              (first position, segment) per 16-row tile
  *   tiles_large [2T]              (first position, segment) per 64-row tile
  * Only the first n_active / S / S+1 / n_tiles entries are meaningful.
+ * There is no per-segment rank array: every kernel reads the rank of segment
+ * s as slot_rank[seg_adapter[s]] from the pool's device metadata when it
+ * runs, so one build stays valid when a slot is refilled with an adapter of
+ * another rank ("LoRAForge" 4.1 and 5: each slot's retained rank lives in
+ * device metadata at a fixed address).
  */
 size_t lora_segment_words(int32_t T);
 
@@ -179,6 +188,8 @@ size_t lora_segment_words(int32_t T);
  *
  *   ids      host int32 [T]: adapter id per row, -1 = no adapter
  *   active   host uint8 [T] or NULL (NULL = every row with id >= 0 is live)
+ *   n_slots  the pool's slot count, the only part of a pool the grouping
+ *            needs (ids are checked against it; ranks are not read here)
  *   order    0: segments by ascending adapter id (canonical);
  *            1: segments in order of first appearance in the batch
  *            (the book's printed example).  Rows keep batch order inside a
@@ -295,9 +306,16 @@ int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const in
                       int32_t d_in, int32_t d_out, int32_t flags, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Workspace bytes lora_fused_linear needs for this call shape (with or
- * without an adapter pool; the size with a pool covers both). */
+/* Workspace bytes lora_fused_linear needs for this call shape, whatever the
+ * pool: the largest need over every rank capacity 1 .. LORA_MAX_RANK and over
+ * the base product alone (the schedule depends on the pool's capacity, whose
+ * rank-r v rows and B slices share the LDS with the main loop's ring).  This
+ * stands in for a generic workspace query taking the call's descriptors: the
+ * fused calls are the only ones that need a workspace. */
 size_t lora_fused_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags);
+/* The exact need of a call with a pool of rank capacity r_cap (0 = no pool). */
+size_t lora_fused_workspace_bytes_rcap(int32_t T, int32_t d_in, int32_t d_out, int32_t base_dtype, int32_t flags,
+                                       int32_t r_cap);
 
 /*
  * Fused linear over several output slices of one input in one launch

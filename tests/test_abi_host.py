@@ -224,11 +224,13 @@ def test_quant_and_dev_builder_validation():
     assert lib.lora_build_segments_dev(None, None, 8, 4, 0, FAKE, None) == agm.LORA_E_ARG
     # bf16 filling the GPU exactly once (256 tiles of 64 x 64): no workspace;
     # more 128-row tiles than CUs (3 x 96 of 128 x 128): 64 bytes of claim
-    # counters; 256-row tiles (16 x 128 of 256 x 256) stay one-shot;
+    # counters; 256-row tiles (16 x 128 of 256 x 256) stay one-shot for small
+    # rank capacities, but pools of capacity >= 96 leave no LDS for them and
+    # take persistent 128 x 128 tiles: the query covers every capacity;
     # fp8 W8A8: codes + scales
     assert lib.lora_fused_workspace_bytes(256, 64, 4096, agm.BF16, 0) == 0
     assert lib.lora_fused_workspace_bytes(384, 64, 12288, agm.BF16, 0) == 64
-    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 0
+    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 64
     assert lib.lora_fused_workspace_bytes(4, 64, 64, agm.FP8_E4M3, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16
     # a small output (10 tiles of 64 x 64): 2 k splits + 1 adapter split per tile
     assert lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0) == 10 * 3 * 64 * 64 * 4 + 10 * 4
@@ -346,3 +348,36 @@ def test_cu_masked_stream_argument_errors():
     assert agm.cu_mask_words([0, 31, 32, 255], 256) == [0x80000001, 1, 0, 0, 0, 0, 0, 0x80000000]
     with pytest.raises(ValueError):
         agm.cu_mask_words([256], 256)
+
+
+@pytest.mark.parametrize("r_cap", [0, 8, 16, 64, 96, 128])
+def test_fused_workspace_query_covers_every_rank_capacity(r_cap):
+    """The size query takes no pool, so it must cover the schedule of any
+    rank capacity.  The exact need of a capacity is checked against the call
+    itself without launching anything: only shapes that need a workspace are
+    called, one byte short (LORA_E_SIZE) and with enough bytes at a
+    deliberately misaligned address (LORA_E_ALIGN, after the size check)."""
+    lib = agm.lib()
+    fake = 1 << 20
+    for (T, d_in, d_out) in [(2048, 4096, 4096), (8192, 4096, 28672), (256, 4096, 4096), (100, 1024, 264),
+                             (512, 8192, 28672)]:
+        any_cap = lib.lora_fused_workspace_bytes(T, d_in, d_out, agm.BF16, 0)
+        need = lib.lora_fused_workspace_bytes_rcap(T, d_in, d_out, agm.BF16, 0, r_cap)
+        assert any_cap >= need
+        if need == 0:
+            continue                      # a complete call would launch: not made here
+        pool = agm.PoolDesc(fake, fake, fake, fake, agm.BF16, 64, r_cap, d_in, d_out) if r_cap else None
+        base = agm.BaseDesc(fake, None, agm.BF16, d_in)
+
+        def call(ws, nbytes):
+            return lib.lora_fused_linear(ctypes.byref(base), ctypes.byref(pool) if pool else None,
+                                         fake if pool else None, T, 2 * fake, d_in, 3 * fake if pool else None,
+                                         max(r_cap, 4), 4 * fake, d_out, d_in, d_out, 0, ws, nbytes, None)
+        assert call(fake, need - 1) == agm.LORA_E_SIZE
+        assert call(fake + 16, need) == agm.LORA_E_ALIGN
+        assert call(fake + 16, any_cap) == agm.LORA_E_ALIGN
+    # the 2048-row 4096 -> 4096 shape at capacity 128 runs persistent 128 x 128
+    # tiles with 64 bytes of claim counters, which capacity 8 does not need
+    assert lib.lora_fused_workspace_bytes_rcap(2048, 4096, 4096, agm.BF16, 0, 128) == 64
+    assert lib.lora_fused_workspace_bytes_rcap(2048, 4096, 4096, agm.BF16, 0, 8) == 0
+    assert lib.lora_fused_workspace_bytes(2048, 4096, 4096, agm.BF16, 0) == 64

@@ -252,3 +252,144 @@ def test_pins_accept_the_oracle():
 @pytest.mark.parametrize("mutant", _mutants(), ids=lambda f: f.__name__)
 def test_pins_catch_planted_mistakes(mutant):
     assert not _pins_pass(mutant)
+
+
+# --- W8A8: per-token activation quantisation in the base product ------------
+#
+# EpiLoRA 2 and Fig. 4(a): y = (x_q W_q^T) s_x s_w for the base; 3 (K1, K2):
+# the adapter's down-projection uses the unquantised activations.  Pinned by
+# a hand-worked example (tests/golden/w8a8_hand_example.txt), by a closed
+# form (rows that quantise exactly give the W8A16 result bit for bit), by the
+# e4m3 rounding bound, and by planted mistakes that these pins must reject.
+
+def _w8a8_hand():
+    g = load("w8a8_hand_example.txt")
+    codes = g["w_codes"].astype(np.uint8)
+    s_w = g["w_scale"].astype(np.float32)
+    A = np.asarray(g["A0"], np.float64).reshape(1, 1, 2)
+    Bt = np.asarray(g["B0"], np.float64).reshape(1, 2, 1)
+    ids = np.array([0, 0])
+    act = np.array([1, 1], np.uint8)
+    return g, codes, s_w, ids, act, A, Bt, np.array([1]), np.array([g["scale"]])
+
+
+def test_w8a8_hand_example():
+    g, codes, s_w, ids, act, A, Bt, rank, scale = _w8a8_hand()
+    q, s_x = L.act_quant_e4m3(g["x"])
+    assert np.array_equal(q, g["x_q_codes"].astype(np.uint8))
+    assert np.array_equal(s_x.astype(np.float64), g["s_x"])
+    y = L.linear_w8a8(g["x"], codes, s_w, ids, act, A, Bt, rank, scale)
+    assert np.array_equal(y, g["y"])
+    # without adapters the same call is the base product alone
+    y0 = L.linear_w8a8(g["x"], codes, s_w, np.full(2, -1), act, A, Bt, rank, scale)
+    assert np.array_equal(y0, g["base"])
+
+
+def _exact_rows_case(seed=11, T=6, d_in=32, d_out=12):
+    """Rows whose values are e4m3 values times 2^k with amax 448 * 2^k: each
+    quantises exactly (s_x = 2^k, x / s_x on the e4m3 grid)."""
+    from lora_inputs import e4m3_quantise_rows
+    g = np.random.default_rng(seed)
+    grid = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))          # 0 .. 448
+    x = np.empty((T, d_in))
+    for i in range(T):
+        v = g.choice(grid, d_in) * np.where(g.uniform(size=d_in) < 0.5, -1.0, 1.0)
+        v[g.integers(d_in)] = 448.0 * (1 if i % 2 else -1)
+        x[i] = v * 2.0 ** int(g.integers(-12, 3))
+    codes, s_w = e4m3_quantise_rows((g.standard_normal((d_out, d_in)) * 0.02).astype(np.float32))
+    N, R = 3, 4
+    rank = np.array([4, 2, 3])
+    A = np.full((N, R, d_in), np.nan)
+    Bt = np.full((N, d_out, R), np.nan)
+    for a in range(N):
+        A[a, :rank[a]] = g.standard_normal((rank[a], d_in))
+        Bt[a, :, :rank[a]] = g.standard_normal((d_out, rank[a]))
+    ids = np.array([0, 2, -1, 1, 0, 2])[:T]
+    act = np.array([1, 1, 1, 0, 1, 1], np.uint8)[:T]
+    return x, codes, s_w, ids, act, A, Bt, rank, np.array([0.5, 2.0, -1.0])
+
+
+def test_w8a8_exact_rows_equal_w8a16():
+    x, codes, s_w, ids, act, A, Bt, rank, scale = _exact_rows_case()
+    y8 = L.linear_w8a8(x, codes, s_w, ids, act, A, Bt, rank, scale)
+    y16 = L.linear(x, (codes, s_w), ids, act, A, Bt, rank, scale)
+    assert np.array_equal(y8, y16)
+
+
+def test_w8a8_within_the_e4m3_rounding_bound():
+    # |x - x_q| <= 2^-4 |x| (3 mantissa bits, round to nearest) + 2^-10 s_x
+    # (half the subnormal spacing 2^-9), so the base moves by at most
+    # sum_k |x_k - x_q,k| |W_nk|; the adapter term is unchanged.
+    from lora_inputs import e4m3_quantise_rows
+    g = np.random.default_rng(12)
+    T, d_in, d_out = 9, 48, 10
+    x = g.standard_normal((T, d_in)) * np.exp(g.uniform(-6, 6, (T, 1)))
+    x = x.astype(np.float32).astype(np.float64)
+    codes, s_w = e4m3_quantise_rows((g.standard_normal((d_out, d_in)) * 0.02).astype(np.float32))
+    W = oracle.decode_e4m3(codes) * s_w.astype(np.float64)[:, None]
+    N, R = 2, 2
+    A = g.standard_normal((N, R, d_in))
+    Bt = g.standard_normal((N, d_out, R))
+    rank, scale = np.array([2, 1]), np.array([1.5, -0.5])
+    ids = g.integers(-1, N, T)
+    y8 = L.linear_w8a8(x, codes, s_w, ids, None, A, Bt, rank, scale)
+    y16 = L.linear(x, (codes, s_w), ids, None, A, Bt, rank, scale)
+    s_x = np.abs(x).max(axis=1) / 448.0
+    bound = (2.0 ** -4 * np.abs(x) + 2.0 ** -10 * s_x[:, None]) @ np.abs(W).T
+    assert np.all(np.abs(y8 - y16) <= bound * (1 + 1e-6))
+    # the bound is not vacuous: the two differ somewhere
+    assert np.abs(y8 - y16).max() > 0
+
+
+def _w8a8_mutants():
+    decode = oracle.decode_e4m3
+
+    def lora_from_xq(x, codes, s_w, ids, act, A, Bt, rank, scale):
+        q, s_x = L.act_quant_e4m3(x)
+        xq = decode(q) * s_x.astype(np.float64)[:, None]
+        return xq @ L.dequant_e4m3_rows(codes, s_w).T + L.lora_delta(xq, ids, act, A, Bt, rank, scale)
+
+    def s_x_wrong_axis(x, codes, s_w, ids, act, A, Bt, rank, scale):
+        q, s_x = L.act_quant_e4m3(x)
+        xq = decode(q) * s_x.astype(np.float64)[None, :]
+        return xq @ L.dequant_e4m3_rows(codes, s_w).T + L.lora_delta(x, ids, act, A, Bt, rank, scale)
+
+    def no_s_w(x, codes, s_w, ids, act, A, Bt, rank, scale):
+        q, s_x = L.act_quant_e4m3(x)
+        xq = decode(q) * s_x.astype(np.float64)[:, None]
+        return xq @ decode(codes).T + L.lora_delta(x, ids, act, A, Bt, rank, scale)
+
+    def no_s_x(x, codes, s_w, ids, act, A, Bt, rank, scale):
+        q, _ = L.act_quant_e4m3(x)
+        return decode(q) @ L.dequant_e4m3_rows(codes, s_w).T + L.lora_delta(x, ids, act, A, Bt, rank, scale)
+
+    def unquantised(x, codes, s_w, ids, act, A, Bt, rank, scale):
+        return L.linear(x, (codes, s_w), ids, act, A, Bt, rank, scale)
+
+    def no_adapter(x, codes, s_w, ids, act, A, Bt, rank, scale):
+        q, s_x = L.act_quant_e4m3(x)
+        xq = decode(q) * s_x.astype(np.float64)[:, None]
+        return xq @ L.dequant_e4m3_rows(codes, s_w).T
+
+    return [lora_from_xq, s_x_wrong_axis, no_s_w, no_s_x, unquantised, no_adapter]
+
+
+def _w8a8_pins_pass(fn):
+    g, codes, s_w, ids, act, A, Bt, rank, scale = _w8a8_hand()
+    try:
+        if not np.array_equal(fn(g["x"], codes, s_w, ids, act, A, Bt, rank, scale), g["y"]):
+            return False
+        x, codes, s_w, ids, act, A, Bt, rank, scale = _exact_rows_case()
+        y = fn(x, codes, s_w, ids, act, A, Bt, rank, scale)
+        return bool(np.array_equal(y, L.linear(x, (codes, s_w), ids, act, A, Bt, rank, scale)))
+    except Exception:
+        return False
+
+
+def test_w8a8_pins_accept_the_oracle():
+    assert _w8a8_pins_pass(L.linear_w8a8)
+
+
+@pytest.mark.parametrize("mutant", _w8a8_mutants(), ids=lambda f: f.__name__)
+def test_w8a8_pins_catch_planted_mistakes(mutant):
+    assert not _w8a8_pins_pass(mutant)

@@ -92,6 +92,14 @@ def test_lorazor_printed_launch_examples():
     assert oracle.tiles_exact([rows], BM) == int(g["tiles_needed"])
     assert oracle.tiles_full_batch(1, M, BM) == int(g["tiles_full_batch_per_slot"])
     assert oracle.row_bound_set(M) == list(g["row_bound_set"].astype(int))
+    # Eq. 3's row dimension under the shared bound, worked from the same page
+    # numbers (a mistake that uses M, or m_max, for R fails here)
+    for k in ("a", "b"):
+        R = oracle.row_bound(M, int(g[f"m_max_{k}"]))
+        assert R == int(g[f"R_{k}"])
+        per_slot = int(g[f"shared_bound_tiles_per_slot_{k}"])
+        assert oracle.tiles_shared_bound(1, R, BM) == per_slot
+        assert oracle.tiles_shared_bound(7, R, BM) == 7 * per_slot
 
 
 def test_row_bound_rules():
