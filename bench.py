@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the multi-adapter linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--w8a8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--configs all|none|a,b]
 
 One step is one pass of the whole hot path over one batch: device-side
 segment build -> shrink -> fused linear (base GEMM with the adapter
@@ -13,8 +13,16 @@ Inputs are resident in HBM before timing; several copies of every buffer
 are rotated so that a step never finds its operands in the 256 MB
 Infinity Cache.  Prints one JSON line.
 
-The default workload is the decode batch (Llama-3-8B q_proj 4096->4096,
-bf16, 256 tokens, 64 slots of rank 16); --config selects another.
+The headline (`value`, `roofline`) is the prefill batch, the largest
+workload by work (fused gate+up 4096->28672, bf16, 8192 tokens in 32
+requests, 128 slots of ranks 8..64); --config selects another.  After it,
+every workload is measured once more into `per_config` (fewer steps): the
+fused path with its kernel times and roofline, for the fp8 workload both
+W8A16 and W8A8, for the decode batch the unfused shrink + expand in every
+launch-sizing mode against the HBM roofline, and for the Llama layer set
+the launch-sizing modes of the unfused adapter term.  `cpu_baseline` is the
+fp64 oracle on the host's cores (and on one thread for the two smallest
+workloads), with the CPU model.
 """
 from __future__ import annotations
 
@@ -42,9 +50,15 @@ METRIC = "multi-LoRA linear tokens/s; achieved HBM GB/s (decode) & MFMA % (prefi
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="decode_bgmv")
+    ap.add_argument("--config", default="prefill_sgmv", choices=ALL_CONFIGS,
+                    help="the headline workload (default: the prefill batch, the largest by work)")
+    ap.add_argument("--configs", default="all",
+                    help="workloads measured after the headline, one per_config entry each: 'all', 'none' or a "
+                         "comma-separated list")
+    ap.add_argument("--cpu-seconds-config", type=float, default=2.0,
+                    help="oracle seconds per workload in cpu_baseline.per_config")
     ap.add_argument("--w8a8", action="store_true", help="fp8 base: quantise activations per token")
     ap.add_argument("--no-slices", action="store_true",
                     help="one fused call per projection (default: projections of one input share a call)")
@@ -139,6 +153,378 @@ def stored_traffic(workload: str):
     return int(float(kv["traffic_bytes_per_launch"]))
 
 
+ALL_CONFIGS = ["tiny_sgmv", "decode_bgmv", "prefill_sgmv", "fp8_fused", "llama_layer"]
+
+
+class Setup:
+    """One workload on the device: every projection's base weight, adapter
+    pool (only the slots the batch touches are filled; the others are zero
+    and never read), input, output and v buffers, rotated over copies whose
+    total exceeds twice the 256 MB Infinity Cache, plus the ids, the segment
+    buffers and the fused workspaces of every copy."""
+
+    def __init__(self, name: str, args, flags_list=(0,)):
+        import torch
+        import adapter_gemm_amd as agm
+        from lora_inputs import make_workload
+        dev = "cuda:0"
+        self.agm = agm
+        w = make_workload(name)
+        self.w, self.T = w, w.T
+        T = w.T
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        touched = w.touched_slots()
+        projs, inst_bytes = [], 0
+        for p in w.projections:
+            A, B = p.pool(touched)
+            pr = {"p": p}
+            mk = bf16 if p.data_dtype == "bf16" else (lambda a: torch.from_numpy(a).to(dev))
+            pr["A"], pr["B"] = mk(A), mk(B)
+            del A, B
+            w0 = p.w0()
+            if p.base_dtype == "fp8":
+                pr["W"], pr["ws"] = torch.from_numpy(w0[0]).to(dev), torch.from_numpy(w0[1]).to(dev)
+            else:
+                pr["W"], pr["ws"] = mk(w0), None
+            del w0
+            pr["x"] = mk(w.x(p))
+            pr["rank"] = torch.from_numpy(p.slot_rank).to(dev)
+            pr["scale"] = torch.from_numpy(p.slot_scale).to(dev)
+            ydt = torch.bfloat16 if p.data_dtype == "bf16" else torch.float32
+            pr["y"] = torch.empty(T, p.d_out, dtype=ydt, device=dev)
+            pr["v"] = torch.empty(T, p.r_cap, dtype=torch.float32, device=dev)
+            for k in ("A", "B", "W", "x", "y", "v"):
+                inst_bytes += pr[k].numel() * pr[k].element_size()
+            projs.append(pr)
+        ids = torch.from_numpy(w.ids).to(dev)
+        act = torch.from_numpy(w.active).to(dev)
+        self.n_slots = w.projections[0].n_slots
+        self.names = [p.name for p in w.projections]
+        self.inst_bytes = inst_bytes
+        n_rot = min(64, max(1, -(-2 * CACHE_BYTES // max(inst_bytes, 1))))
+        self.n_rot = n_rot
+        self.insts = []
+        bt_of = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}
+        for r in range(n_rot):
+            inst = []
+            for pr in projs:
+                c = {k: (pr[k] if r == 0 else pr[k].clone()) if isinstance(pr[k], torch.Tensor) else pr[k]
+                     for k in pr}
+                c["pool"] = agm.pool_desc(c["A"], c["B"], c["rank"], c["scale"])
+                c["base"] = agm.base_desc(c["W"], c["ws"])
+                p = c["p"]
+                c["wsp"] = {f: agm.fused_workspace(T, p.d_in, p.d_out, bt_of[p.base_dtype], f, device=dev)
+                            for f in flags_list}
+                inst.append(c)
+            seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=dev)
+            self.insts.append({"inst": inst, "seg": seg, "ids": ids.clone(), "act": act.clone(), "gws": {}})
+        self.bt_of = bt_of
+        torch.cuda.synchronize()
+        print(f"# {name}: {w.description}; {n_rot} rotated instance(s) of {inst_bytes / 1e6:.1f} MB",
+              file=sys.stderr, flush=True)
+
+    def groups(self, slices: bool):
+        if self.w.name in SLICE_GROUPS and slices:
+            return [[self.names.index(n) for n in g] for g in SLICE_GROUPS[self.w.name]]
+        return [[j] for j in range(len(self.names))]
+
+    def group_workspaces(self, groups, flags):
+        import torch
+        for it in self.insts:
+            key = (tuple(map(tuple, groups)), flags)
+            if key in it["gws"]:
+                continue
+            gws = []
+            for g in groups:
+                p0 = it["inst"][g[0]]["p"]
+                gws.append(self.agm.fused_slices_workspace(self.T, p0.d_in, [it["inst"][j]["p"].d_out for j in g],
+                                                           self.bt_of[p0.base_dtype], flags, device="cuda:0")
+                           if len(g) > 1 else None)
+            it["gws"][key] = gws
+        torch.cuda.synchronize()
+
+    def release(self):
+        import torch
+        self.insts = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def ev_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def algorithmic(S: Setup, groups):
+    """Bytes and flops the method must move and do (each distinct live
+    adapter's A and B once at its true rank, x once per input, v at fp32,
+    y written once, W0 at its stored width)."""
+    w, T = S.w, S.T
+    live = w.live()
+    n_act = int(live.sum())
+    alg = {"fused_bytes": 0, "fused_flops": 0, "shrink_bytes": 0, "shrink_flops": 0, "expand_bytes": 0,
+           "expand_flops": 0, "per_group_bytes": [], "per_group_flops": []}
+    first_of_group = {g[0] for g in groups}
+    per_proj = []
+    for jp, p in enumerate(w.projections):
+        el = 2 if p.data_dtype == "bf16" else 4
+        wel = 1 if p.base_dtype == "fp8" else (2 if p.base_dtype == "bf16" else 4)
+        used = sorted(set(int(a) for a in w.ids[live]))
+        ranks = np.array([int(p.slot_rank[a]) for a in used], dtype=np.int64)
+        rows_r = np.array([int(p.slot_rank[a]) for a in w.ids[live]], dtype=np.int64)
+        adapters_A = int((ranks * p.d_in).sum()) * el
+        adapters_B = int((ranks * p.d_out).sum()) * el
+        v_bytes = int(rows_r.sum()) * 4
+        x_once = T * p.d_in * el if jp in first_of_group else 0
+        fb = (p.d_out * p.d_in * wel + (4 * p.d_out if p.base_dtype == "fp8" else 0) + x_once + T * p.d_out * el
+              + adapters_B + v_bytes)
+        ff = 2 * T * p.d_in * p.d_out + 2 * int(rows_r.sum()) * p.d_out
+        per_proj.append((fb, ff))
+        alg["fused_bytes"] += fb
+        alg["fused_flops"] += ff
+        alg["shrink_bytes"] += adapters_A + n_act * p.d_in * el + v_bytes
+        alg["shrink_flops"] += 2 * int(rows_r.sum()) * p.d_in
+        # the unfused expand reads B and v and reads and writes the live rows of y
+        alg["expand_bytes"] += adapters_B + v_bytes + 2 * n_act * p.d_out * el
+        alg["expand_flops"] += 2 * int(rows_r.sum()) * p.d_out
+    for g in groups:
+        alg["per_group_bytes"].append(sum(per_proj[j][0] for j in g))
+        alg["per_group_flops"].append(sum(per_proj[j][1] for j in g))
+    alg["n_active"] = n_act
+    return alg
+
+
+def roofline(bytes_, flops, seconds, base, mfma_dtype, kernel, traffic_key, launches):
+    ridge = MFMA_PEAK_TFLOPS[mfma_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ai = flops / bytes_
+    gbs = bytes_ / seconds / 1e9
+    tfs = flops / seconds / 1e12
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        pk = MFMA_PEAK_TFLOPS[mfma_dtype]
+        roof = {"bound": "alu" if base == "fp32" else "mfma", "achieved": round(tfs, 1), "peak": pk,
+                "unit": "TFLOP/s", "frac": round(tfs / pk, 4)}
+    roof["kernel"] = kernel
+    roof["algorithmic_bytes_per_launch"] = bytes_ // launches
+    roof["algorithmic_flops_per_launch"] = flops // launches
+    tr = stored_traffic(traffic_key)
+    roof["traffic"] = tr
+    roof["traffic_over_algorithmic"] = None if tr is None else round(tr / (bytes_ / launches), 3)
+    return roof
+
+
+def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, separate_build: bool):
+    """The whole hot path, one step per batch: device segment build -> shrink
+    -> fused linear for every projection (projections of one input share a
+    sliced launch).  Returns the step time from K back-to-back steps between
+    two events, and each kernel's duration from a second run of K steps with
+    events around every launch (on the stream the library launches on)."""
+    import torch
+    agm, T = S.agm, S.T
+    groups = S.groups(slices)
+    S.group_workspaces(groups, flags)
+    n_proj, n_groups = len(S.names), len(groups)
+    combined = not separate_build and 1 <= T <= 256 and S.n_slots <= 1024
+    j_first = groups[0][0]
+    stream = torch.cuda.current_stream()
+    gkey = (tuple(map(tuple, groups)), flags)
+
+    def step(i, ev=None):
+        it = S.insts[i % S.n_rot]
+        inst, seg = it["inst"], it["seg"]
+        if ev is not None:
+            ev["seg"][0].record(stream)
+        if combined:
+            c = inst[j_first]
+            agm.build_shrink_dev(it["ids"], it["act"], c["pool"], seg, c["x"], c["v"])
+        else:
+            agm.build_segments_dev(it["ids"], it["act"], S.n_slots, seg)
+        if ev is not None:
+            ev["seg"][1].record(stream)
+        for gi, g in enumerate(groups):
+            x = inst[g[0]]["x"]
+            for j in g:
+                if combined and j == j_first:
+                    continue
+                c = inst[j]
+                if ev is not None:
+                    ev["shrink"][j][0].record(stream)
+                agm.shrink(c["pool"], seg, T, None, x, c["v"], launch=agm.LAUNCH_PERSISTENT)
+                if ev is not None:
+                    ev["shrink"][j][1].record(stream)
+            if ev is not None:
+                ev["fused"][gi][0].record(stream)
+            if len(g) == 1:
+                c = inst[g[0]]
+                agm.fused_linear(c["base"], c["pool"], seg, x, c["v"], c["y"], flags=flags, workspace=c["wsp"][flags])
+            else:
+                agm.fused_linear_slices([inst[j]["base"] for j in g], [inst[j]["pool"] for j in g], seg, x,
+                                        [inst[j]["v"] for j in g], [inst[j]["y"] for j in g], flags=flags,
+                                        workspace=it["gws"][gkey][gi])
+            if ev is not None:
+                ev["fused"][gi][1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = ev_pair()
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    evs = [{"seg": ev_pair(), "shrink": [ev_pair() for _ in range(n_proj)],
+            "fused": [ev_pair() for _ in range(n_groups)]} for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    per = {"seg": 0.0, "shrink": 0.0, "fused": 0.0}
+    fused_each = [0.0] * n_groups
+    for ev in evs:
+        per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
+        for j in range(n_proj):
+            if not (combined and j == j_first):
+                per["shrink"] += ev["shrink"][j][0].elapsed_time(ev["shrink"][j][1])
+        for gi in range(n_groups):
+            d = ev["fused"][gi][0].elapsed_time(ev["fused"][gi][1])
+            per["fused"] += d
+            fused_each[gi] += d
+    per = {k: v / steps for k, v in per.items()}
+    fused_each = [v / steps for v in fused_each]
+
+    alg = algorithmic(S, groups)
+    base = S.w.projections[0].base_dtype
+    w8a8 = bool(flags & agm.FLAG_ACT_QUANT_E4M3)
+    mfma_dtype = "fp8" if (base == "fp8" and w8a8) else ("fp32" if base == "fp32" else "bf16")
+    roof = roofline(alg["fused_bytes"], alg["fused_flops"], per["fused"] * 1e-3, base, mfma_dtype,
+                    "fused_f32_kernel" if base == "fp32" else DOMINANT, S.w.name + ("_w8a8" if w8a8 else ""),
+                    n_groups)
+    shrink_s = (per["shrink"] + (per["seg"] if combined else 0.0)) * 1e-3
+    shrink_gbs = alg["shrink_bytes"] / shrink_s / 1e9
+    names = S.names
+    return {
+        "ms_per_step": ms_step,
+        "value": T / (ms_step * 1e-3),
+        "combined": combined,
+        "groups": groups,
+        "path": ("build_shrink_dev (one launch)" if combined else "build_segments_dev -> shrink (persistent)")
+                + " -> fused_linear"
+                + (" (one sliced launch per group: " + ", ".join("/".join(names[j] for j in g)
+                                                                for g in groups if len(g) > 1) + ")"
+                   if any(len(g) > 1 for g in groups) else "")
+                + (" W8A8" if w8a8 else (" W8A16" if base == "fp8" else "")),
+        "mfma_dtype": mfma_dtype,
+        "roofline": roof,
+        "kernels_us_per_step": {("build_shrink" if combined else "build_segments"): round(per["seg"] * 1e3, 2),
+                                ("shrink_others" if combined else "shrink"): round(per["shrink"] * 1e3, 2),
+                                "fused_linear": round(per["fused"] * 1e3, 2)},
+        "fused_us_per_launch": {"/".join(names[j] for j in g): round(fused_each[gi] * 1e3, 2)
+                                for gi, g in enumerate(groups)},
+        "shrink_hbm": {"achieved": round(shrink_gbs, 1), "unit": "GB/s", "frac": round(shrink_gbs / HBM_PEAK_GBS, 4),
+                       "algorithmic_bytes": alg["shrink_bytes"], "includes_segment_build": combined},
+        "alg": alg,
+    }
+
+
+def unfused_adapter(S: Setup, steps: int, warmup: int, modes):
+    """The adapter term without fusion: lora_shrink then lora_expand (y += s B v
+    in place) for every projection, per launch-sizing mode ("LoRazor" 3.1.1-3.1.2:
+    the exact tile list, the shared row bound R and the full-batch bound).  The
+    segment buffer is built once per rotated copy (host planner, which also
+    gives EXACT and BUCKETED their host summary); each mode's K steps run back
+    to back with events around every launch.  Row tiles launched and holding
+    rows are counted from the summary: exact sum_a ceil(m_a/16), bucketed
+    L ceil(R/16), full batch L ceil(T/16) with L = min(T, slots)."""
+    import torch
+    agm, T = S.agm, S.T
+    stream = torch.cuda.current_stream()
+    summaries = []
+    for it in S.insts:
+        staging = torch.empty(agm.segment_words(T), dtype=torch.int32).pin_memory()
+        summaries.append(agm.build_segments(torch.from_numpy(S.w.ids), torch.from_numpy(S.w.active), S.n_slots,
+                                            it["seg"], staging))
+        torch.cuda.synchronize()
+    s0 = summaries[0]
+    L = min(T, S.n_slots)
+    tiles = {agm.LAUNCH_EXACT: s0.n_tiles_small, agm.LAUNCH_PERSISTENT: s0.n_tiles_small,
+             agm.LAUNCH_BUCKETED: L * -(-s0.row_bound // 16), agm.LAUNCH_FULL_BATCH: L * -(-T // 16)}
+    mode_name = {agm.LAUNCH_EXACT: "exact", agm.LAUNCH_PERSISTENT: "persistent", agm.LAUNCH_BUCKETED: "bucketed",
+                 agm.LAUNCH_FULL_BATCH: "full_batch"}
+    alg = algorithmic(S, [[j] for j in range(len(S.names))])
+    out = {"row_tiles_with_rows": s0.n_tiles_small, "row_bound": s0.row_bound, "slots_L": L, "modes": []}
+    for mode in modes:
+        def step(i, ev=None):
+            it = S.insts[i % S.n_rot]
+            summ = summaries[i % S.n_rot]
+            for c in it["inst"]:
+                if ev is not None:
+                    ev[0].record(stream)
+                agm.shrink(c["pool"], it["seg"], T, summ, c["x"], c["v"], launch=mode)
+                if ev is not None:
+                    ev[1].record(stream)
+                agm.expand(c["pool"], it["seg"], T, summ, c["v"], c["y"], launch=mode)
+                if ev is not None:
+                    ev[2].record(stream)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0, t1 = ev_pair()
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        pair_ms = t0.elapsed_time(t1) / steps
+        evs = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in S.names]
+               for _ in range(steps)]
+        sh = ex = 0.0
+        for i in range(steps):
+            it_evs = evs[i]
+            it = S.insts[i % S.n_rot]
+            summ = summaries[i % S.n_rot]
+            for c, e in zip(it["inst"], it_evs):
+                e[0].record(stream)
+                agm.shrink(c["pool"], it["seg"], T, summ, c["x"], c["v"], launch=mode)
+                e[1].record(stream)
+                agm.expand(c["pool"], it["seg"], T, summ, c["v"], c["y"], launch=mode)
+                e[2].record(stream)
+        torch.cuda.synchronize()
+        for it_evs in evs:
+            for e in it_evs:
+                sh += e[0].elapsed_time(e[1])
+                ex += e[1].elapsed_time(e[2])
+        sh, ex = sh / steps * 1e-3, ex / steps * 1e-3           # seconds per step
+        both = alg["shrink_bytes"] + alg["expand_bytes"]
+        out["modes"].append({
+            "mode": mode_name[mode], "row_tiles_launched": int(tiles[mode]),
+            "shrink_us": round(sh * 1e6, 2), "expand_us": round(ex * 1e6, 2),
+            "shrink_expand_us": round(pair_ms * 1e3, 2),
+            "shrink_hbm_frac": round(alg["shrink_bytes"] / sh / 1e9 / HBM_PEAK_GBS, 4),
+            "expand_hbm_frac": round(alg["expand_bytes"] / ex / 1e9 / HBM_PEAK_GBS, 4),
+            "pair_hbm_frac": round(both / (pair_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    out["algorithmic_bytes"] = {"shrink": alg["shrink_bytes"], "expand": alg["expand_bytes"]}
+    out["target_hbm_frac"] = 0.70
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     args = parse()
     if args.counter_summary:
@@ -153,250 +539,101 @@ def main():
 
     import torch
     import adapter_gemm_amd as agm
-    from lora_inputs import make_workload
-
-    dev = "cuda:0"
     torch.cuda.set_device(0)
-    w = make_workload(args.config)
-    T = w.T
-    print(f"# workload {w.name}: {w.description}", file=sys.stderr, flush=True)
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    # ---- one instance on the device ------------------------------------
-    touched = w.touched_slots()
-    projs = []
-    inst_bytes = 0
-    for p in w.projections:
-        A, B = p.pool(touched)            # untouched slots stay zero: never read
-        pr = {"p": p}
-        pr["A"], pr["B"] = bf16(A) if p.data_dtype == "bf16" else torch.from_numpy(A).to(dev), \
-            bf16(B) if p.data_dtype == "bf16" else torch.from_numpy(B).to(dev)
-        del A, B
-        w0 = p.w0()
-        if p.base_dtype == "fp8":
-            pr["W"], pr["ws"] = torch.from_numpy(w0[0]).to(dev), torch.from_numpy(w0[1]).to(dev)
-        elif p.base_dtype == "bf16":
-            pr["W"], pr["ws"] = bf16(w0), None
-        else:
-            pr["W"], pr["ws"] = torch.from_numpy(w0).to(dev), None
-        del w0
-        x = w.x(p)
-        pr["x"] = bf16(x) if p.data_dtype == "bf16" else torch.from_numpy(x).to(dev)
-        pr["rank"] = torch.from_numpy(p.slot_rank).to(dev)
-        pr["scale"] = torch.from_numpy(p.slot_scale).to(dev)
-        ydt = torch.bfloat16 if p.data_dtype == "bf16" else torch.float32
-        pr["y"] = torch.empty(T, p.d_out, dtype=ydt, device=dev)
-        pr["v"] = torch.empty(T, p.r_cap, dtype=torch.float32, device=dev)
-        for k in ("A", "B", "W", "x", "y", "v"):
-            inst_bytes += pr[k].numel() * pr[k].element_size()
-        projs.append(pr)
-    ids = torch.from_numpy(w.ids).to(dev)
-    act = torch.from_numpy(w.active).to(dev)
-    n_slots = w.projections[0].n_slots
-
-    # ---- rotated copies ------------------------------------------------
-    n_rot = max(1, -(-2 * CACHE_BYTES // max(inst_bytes, 1)))
-    n_rot = min(n_rot, 64)
     flags = agm.FLAG_ACT_QUANT_E4M3 if args.w8a8 else 0
-    names = [p.name for p in w.projections]
-    if w.name in SLICE_GROUPS and not args.no_slices:
-        groups = [[names.index(n) for n in g] for g in SLICE_GROUPS[w.name]]
-    else:
-        groups = [[j] for j in range(len(names))]
-    insts = []
-    for r in range(n_rot):
-        inst = []
-        for pr in projs:
-            c = {k: (pr[k] if r == 0 else pr[k].clone()) if isinstance(pr[k], torch.Tensor) else pr[k]
-                 for k in pr}
-            c["pool"] = agm.pool_desc(c["A"], c["B"], c["rank"], c["scale"])
-            c["base"] = agm.base_desc(c["W"], c["ws"])
-            p = c["p"]
-            bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p.base_dtype]
-            c["wsp"] = agm.fused_workspace(T, p.d_in, p.d_out, bt, flags, device=dev)
-            inst.append(c)
-        gws = []
-        for g in groups:
-            p0 = inst[g[0]]["p"]
-            bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3, "fp32": agm.F32}[p0.base_dtype]
-            gws.append(agm.fused_slices_workspace(T, p0.d_in, [inst[j]["p"].d_out for j in g], bt, flags, device=dev)
-                       if len(g) > 1 else None)
-        seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=dev)
-        insts.append((inst, seg, ids.clone(), act.clone(), gws))
-    torch.cuda.synchronize()
-    print(f"# {n_rot} rotated instance(s) of {inst_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
-    stream = torch.cuda.current_stream()
-    n_proj = len(projs)
     if args.concurrent:
-        concurrent_line(args, w, insts, n_rot, n_slots)
+        S = Setup(args.config, args)
+        concurrent_line(args, S.w, [(it["inst"], it["seg"], it["ids"], it["act"], None) for it in S.insts],
+                        S.n_rot, S.n_slots)
         return
 
-    n_groups = len(groups)
-    # the library's one-launch rule for the segment build with the shrink
-    combined = not args.separate_build and 1 <= T <= 256 and n_slots <= 1024
-    j_first = groups[0][0]
-
-    def step(i, ev=None):
-        inst, seg, ids_d, act_d, gws = insts[i % n_rot]
-        if ev is not None:
-            ev["seg"][0].record(stream)
-        if combined:
-            c = inst[j_first]
-            agm.build_shrink_dev(ids_d, act_d, c["pool"], seg, inst[j_first]["x"], c["v"])
-        else:
-            agm.build_segments_dev(ids_d, act_d, n_slots, seg)
-        if ev is not None:
-            ev["seg"][1].record(stream)
-        for gi, g in enumerate(groups):
-            x = inst[g[0]]["x"]                      # the group's one input
-            for j in g:
-                if combined and j == j_first:
-                    continue                         # its shrink ran in the build launch
-                c = inst[j]
-                if ev is not None:
-                    ev["shrink"][2 * j].record(stream)
-                agm.shrink(c["pool"], seg, T, None, x, c["v"], launch=agm.LAUNCH_PERSISTENT)
-                if ev is not None:
-                    ev["shrink"][2 * j + 1].record(stream)
-            if ev is not None:
-                ev["fused"][2 * gi].record(stream)
-            if len(g) == 1:
-                c = inst[g[0]]
-                agm.fused_linear(c["base"], c["pool"], seg, x, c["v"], c["y"], flags=flags, workspace=c["wsp"])
-            else:
-                agm.fused_linear_slices([inst[j]["base"] for j in g], [inst[j]["pool"] for j in g], seg, x,
-                                        [inst[j]["v"] for j in g], [inst[j]["y"] for j in g], flags=flags,
-                                        workspace=gws[gi])
-            if ev is not None:
-                ev["fused"][2 * gi + 1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K back-to-back steps between two events (the line's value).
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-
-    # The same K steps again with events around every launch, on the stream
-    # the library launches on (torch's current stream), for each kernel's own
-    # duration.  Event packets add gaps between launches, so the step time
-    # above comes from the run without them.
-    def mk(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    evs = [{"seg": mk(2), "shrink": mk(2 * n_proj), "fused": mk(2 * n_groups)} for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    per = {"seg": 0.0, "shrink": 0.0, "fused": 0.0}
-    for ev in evs:
-        per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
-        for j in range(n_proj):
-            if not (combined and j == j_first):   # one event pair per shrink launch
-                per["shrink"] += ev["shrink"][2 * j].elapsed_time(ev["shrink"][2 * j + 1])
-        for gi in range(n_groups):
-            per["fused"] += ev["fused"][2 * gi].elapsed_time(ev["fused"][2 * gi + 1])
-    per = {k: v / args.steps for k, v in per.items()}   # ms per step
-
+    # ---- the headline workload -------------------------------------------
+    S = Setup(args.config, args, flags_list=(flags,))
+    r = fused_path(S, args.steps, args.warmup, flags, not args.no_slices, args.separate_build)
     if args.calibrate_copy_mb:
-        src = torch.empty(args.calibrate_copy_mb << 20, dtype=torch.uint8, device=dev)
+        src = torch.empty(args.calibrate_copy_mb << 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-
-    # ---- algorithmic work --------------------------------------------------
-    live = w.live()
-    n_act = int(live.sum())
-    alg = {"fused_bytes": 0, "fused_flops": 0, "shrink_bytes": 0, "shrink_flops": 0}
-    first_of_group = {g[0] for g in groups}
-    for jp, pr in enumerate(projs):
-        p = pr["p"]
-        el = 2 if p.data_dtype == "bf16" else 4
-        wel = 1 if p.base_dtype == "fp8" else (2 if p.base_dtype == "bf16" else 4)
-        used = sorted(set(int(a) for a in w.ids[live]))
-        ranks = np.array([int(p.slot_rank[a]) for a in used])
-        rows_r = np.array([int(p.slot_rank[a]) for a in w.ids[live]])
-        adapters_A = int((ranks * p.d_in).sum()) * el
-        adapters_B = int((ranks * p.d_out).sum()) * el
-        v_bytes = int(rows_r.sum()) * 4
-        x_once = T * p.d_in * el if jp in first_of_group else 0    # a group reads its input once
-        alg["fused_bytes"] += (p.d_out * p.d_in * wel + (4 * p.d_out if p.base_dtype == "fp8" else 0)
-                               + x_once + T * p.d_out * el + adapters_B + v_bytes)
-        alg["fused_flops"] += 2 * T * p.d_in * p.d_out + 2 * int(rows_r.sum()) * p.d_out
-        alg["shrink_bytes"] += adapters_A + n_act * p.d_in * el + v_bytes
-        alg["shrink_flops"] += 2 * int(rows_r.sum()) * p.d_in
-    fused_s = per["fused"] * 1e-3
-    # (one launch for build and shrink: its time counts as shrink time too)
-    shrink_s = (per["shrink"] + (per["seg"] if combined else 0.0)) * 1e-3
-    fused_gbs = alg["fused_bytes"] / fused_s / 1e9
-    fused_tfs = alg["fused_flops"] / fused_s / 1e12
-    shrink_gbs = alg["shrink_bytes"] / shrink_s / 1e9
-    base = w.projections[0].base_dtype
-    mfma_dtype = "fp8" if (base == "fp8" and args.w8a8) else ("fp32" if base == "fp32" else "bf16")
-    ridge = MFMA_PEAK_TFLOPS[mfma_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
-    ai = alg["fused_flops"] / alg["fused_bytes"]
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(fused_gbs / HBM_PEAK_GBS, 4)}
-    else:
-        # the fp32 path multiplies with vector FMAs (fp32 vector peak), the
-        # others on MFMA at their dtype's dense peak
-        pk = MFMA_PEAK_TFLOPS[mfma_dtype]
-        roof = {"bound": "alu" if base == "fp32" else "mfma", "achieved": round(fused_tfs, 1), "peak": pk,
-                "unit": "TFLOP/s", "frac": round(fused_tfs / pk, 4)}
-    roof["kernel"] = "fused_f32_kernel" if base == "fp32" else DOMINANT
-    roof["algorithmic_bytes_per_launch"] = alg["fused_bytes"] // n_groups
-    roof["algorithmic_flops_per_launch"] = alg["fused_flops"] // n_groups
-    # (a reading belongs to one kernel: the W8A8 option runs another one)
-    roof["traffic"] = stored_traffic(w.name + ("_w8a8" if args.w8a8 else ""))
-
-    value = T / (ms_step * 1e-3)
+    w = S.w
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(r["value"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if mfma_dtype == "fp8" else ("f32" if base == "fp32" else "bf16"),
+        "dtype": "fp8" if r["mfma_dtype"] == "fp8" else ("f32" if r["mfma_dtype"] == "fp32" else "bf16"),
         "data": "synthetic (seeded generators; Llama-shaped; random-init adapters)",
-        "config": {"workload": f"{w.name}: {w.description}",
-                   "path": ("build_shrink_dev (one launch)" if combined
-                            else "build_segments_dev -> shrink (persistent)") + " -> fused_linear"
-                           + (" (one sliced launch per group: " + ", ".join("/".join(names[j] for j in g)
-                                                                           for g in groups if len(g) > 1) + ")"
-                              if any(len(g) > 1 for g in groups) else "")
-                           + (" W8A8" if args.w8a8 else (" W8A16" if base == "fp8" else "")),
-                   "T": T, "projections": n_proj, "fused_launches": n_groups, "live_rows": n_act,
-                   "distinct_adapters": len(w.touched_slots()), "rotated_instances": n_rot},
-        "roofline": roof,
-        "kernels_us_per_step": {("build_shrink" if combined else "build_segments"): round(per["seg"] * 1e3, 2),
-                                ("shrink_others" if combined else "shrink"): round(per["shrink"] * 1e3, 2),
-                                "fused_linear": round(per["fused"] * 1e3, 2)},
-        "shrink_hbm": {"achieved": round(shrink_gbs, 1), "unit": "GB/s",
-                       "frac": round(shrink_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg["shrink_bytes"],
-                       "includes_segment_build": combined},
+        "config": {"workload": f"{w.name}: {w.description}", "path": r["path"], "T": S.T,
+                   "projections": len(S.names), "fused_launches": len(r["groups"]),
+                   "live_rows": r["alg"]["n_active"], "distinct_adapters": len(w.touched_slots()),
+                   "rotated_instances": S.n_rot},
+        "roofline": r["roofline"],
+        "kernels_us_per_step": r["kernels_us_per_step"],
+        "shrink_hbm": r["shrink_hbm"],
     }
+    S.release()
+    del S
+
+    # ---- every workload, one line each (the headline's numbers repeated) ---
+    configs = [] if args.configs == "none" else (ALL_CONFIGS if args.configs == "all" else args.configs.split(","))
+    per_cfg = {}
+    steps_c, warm_c = max(5, min(args.steps, 50)), max(2, min(args.warmup, 10))
+    for name in configs:
+        if name == args.config and not args.w8a8:
+            rr = r
+            entry = _cfg_entry(rr)
+            entry["same_as_headline"] = True
+            per_cfg[name] = entry
+            if name not in ("decode_bgmv", "llama_layer"):
+                continue
+        fl = (0, agm.FLAG_ACT_QUANT_E4M3) if name == "fp8_fused" else (0,)
+        Sc = Setup(name, args, flags_list=fl)
+        if name not in per_cfg:
+            per_cfg[name] = _cfg_entry(fused_path(Sc, steps_c, warm_c, 0, not args.no_slices, args.separate_build))
+        if name == "fp8_fused":
+            per_cfg["fp8_fused_w8a8"] = _cfg_entry(fused_path(Sc, steps_c, warm_c, agm.FLAG_ACT_QUANT_E4M3, True,
+                                                              args.separate_build))
+        if name == "decode_bgmv":
+            per_cfg[name]["unfused_shrink_expand"] = unfused_adapter(
+                Sc, steps_c, warm_c, (agm.LAUNCH_PERSISTENT, agm.LAUNCH_EXACT, agm.LAUNCH_BUCKETED,
+                                      agm.LAUNCH_FULL_BATCH))
+        if name == "llama_layer":
+            per_cfg[name]["launch_sizing"] = unfused_adapter(
+                Sc, max(5, steps_c // 2), warm_c, (agm.LAUNCH_EXACT, agm.LAUNCH_BUCKETED, agm.LAUNCH_FULL_BATCH))
+        Sc.release()
+        del Sc
+    if per_cfg:
+        out["per_config"] = per_cfg
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        from lora_inputs import make_workload
+        out["cpu_baseline"] = cpu_baseline(make_workload(args.config), args.cpu_seconds)
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
+        extra = {}
+        for name in configs:
+            wk = make_workload(name)
+            e = {"threads_all": cpu_baseline(wk, args.cpu_seconds_config)}
+            if name in ("tiny_sgmv", "decode_bgmv"):
+                e["threads_1"] = cpu_baseline(wk, args.cpu_seconds_config, threads=1)
+            extra[name] = {k: {kk: v[kk] for kk in ("value", "unit", "cores", "sample")} for k, v in e.items()}
+        if extra:
+            out["cpu_baseline"]["per_config"] = extra
     print(json.dumps(out), flush=True)
+
+
+def _cfg_entry(r):
+    return {"ms_per_step": round(r["ms_per_step"], 5), "tokens_per_s": round(r["value"], 1),
+            "path": r["path"], "kernels_us_per_step": r["kernels_us_per_step"],
+            "fused_us_per_launch": r["fused_us_per_launch"], "roofline": r["roofline"],
+            "shrink_hbm": r["shrink_hbm"]}
 
 
 def concurrent_line(args, w, insts, n_rot: int, n_slots: int) -> None:
@@ -505,17 +742,20 @@ def concurrent_line(args, w, insts, n_rot: int, n_slots: int) -> None:
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, threads=None):
     """The fp64 oracle (as it stands) on this host's cores, on a bounded
     sample of the same workload: whole batches for as long as `seconds`
-    allows (at least one), or a slice of the rows for large workloads."""
+    allows (at least one), or a slice of the rows for large workloads.
+    `threads` limits the BLAS threads (default: every core this process may
+    run on)."""
     import oracle
     try:
         from threadpoolctl import threadpool_limits, threadpool_info
     except ImportError:                       # pragma: no cover
         threadpool_limits = None
     cores = len(os.sched_getaffinity(0))
-    ctx = threadpool_limits(cores) if threadpool_limits else None
+    want = cores if threads is None else threads
+    ctx = threadpool_limits(want) if threadpool_limits else None
     rows = w.T
     # large workloads: a row slice keeps the sample to ~10-30 s of CPU work
     macs = sum(p.d_in * p.d_out for p in w.projections)
@@ -538,16 +778,16 @@ def cpu_baseline(w, seconds: float):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    threads = cores
+    used = want
     if ctx is not None:
         try:
-            threads = max(i.get("num_threads", cores) for i in threadpool_info()) or cores
+            used = max(i.get("num_threads", want) for i in threadpool_info()) or want
         except Exception:
             pass
         ctx.unregister() if hasattr(ctx, "unregister") else None
-    return {"value": round(rows * n / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(rows * n / dt, 2), "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"{n} pass(es) of the fp64 oracle (segments + {len(w.projections)} projection(s)) "
-                      f"over {rows} of {w.T} rows in {dt:.1f} s"}
+                      f"over {rows} of {w.T} rows of {w.name} in {dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -307,6 +307,33 @@ def test_launch_modes_bitwise_identical(launch):
     assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
 
 
+@pytest.mark.parametrize("launch", [agm.LAUNCH_EXACT, agm.LAUNCH_BUCKETED])
+def test_stale_host_summary_costs_no_rows(launch):
+    """EXACT and BUCKETED size their grids from the host summary but take
+    the work from the device buffer: a summary of another batch of the same
+    T (one live row: one tile, row bound 16) still gives every row."""
+    w = make_workload("llama_layer", **SMALL["llama_layer"])
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, p.n_slots)
+    assert s.n_tiles_small > 1 and s.row_bound > 16
+    stale = agm.Summary(1, 1, 1, 16, 1, 1, w.T, 0)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(2)
+    y0 = torch.randn(w.T, p.d_out, device=DEV, generator=gen).to(torch.bfloat16)
+    outs = []
+    for summ in (s, stale):
+        v = torch.zeros(w.T, p.r_cap, device=DEV)
+        y = y0.clone()
+        agm.shrink(dp.pool, seg, w.T, summ, dp.x, v, launch=launch)
+        agm.expand(dp.pool, seg, w.T, summ, v, y, launch=launch)
+        torch.cuda.synchronize()
+        outs.append((v.cpu(), y.cpu()))
+    n = s.n_active
+    assert torch.equal(outs[0][0][:n], outs[1][0][:n])
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
 def test_expand_leaves_other_rows_bitwise_untouched():
     w = make_workload("decode_bgmv", **SMALL["decode_bgmv"])
     p = w.projections[0]
