@@ -27,7 +27,7 @@ SEG_HEADER = 16
 EXPORTED = [
     "lora_segment_words", "lora_build_segments", "lora_plan_segments", "lora_build_segments_dev",
     "lora_shrink", "lora_build_shrink_dev", "lora_expand", "lora_fused_linear", "lora_fused_workspace_bytes",
-    "lora_fused_workspace_bytes_rcap",
+    "lora_fused_workspace_bytes_rcap", "lora_fused_linear_noalloc",
     "lora_fused_linear_slices", "lora_fused_slices_workspace_bytes",
     "lora_registry_create", "lora_registry_destroy", "lora_registry_acquire", "lora_registry_release",
     "lora_registry_lookup", "lora_registry_stats", "lora_pool_install",
@@ -84,6 +84,7 @@ def _load():
         "lora_fused_linear": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P, SZ, P]),
         "lora_fused_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "lora_fused_workspace_bytes_rcap": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "lora_fused_linear_noalloc": (I32, [P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, I32, P]),
         "lora_fused_linear_slices": (I32, [I32, P, P, P, I32, P, I32, I32, P, P, P, P, P, I32, P, SZ, P]),
         "lora_fused_slices_workspace_bytes": (SZ, [I32, I32, I32, P, I32, I32]),
         "lora_registry_create": (I32, [I32, I32, P]),
@@ -360,6 +361,21 @@ def fused_linear(base: BaseDesc, pool: Optional[PoolDesc], seg, x, v, y, flags: 
                                   x.data_ptr(), _ld(x), _ptr(v), 0 if v is None else _ld(v),
                                   y.data_ptr(), _ld(y), d_in, d_out, flags, _ptr(workspace), ws_bytes,
                                   _stream(stream)), "lora_fused_linear")
+
+
+def fused_linear_noalloc(base: BaseDesc, pool: Optional[PoolDesc], seg, x, v, y, flags: int = 0,
+                         stream=None) -> None:
+    """fused_linear with the library's static per-GPU scratch instead of a
+    workspace (the call allocates nothing; calls on one GPU must not overlap)."""
+    T, d_in = int(x.shape[0]), int(x.shape[1])
+    d_out = int(y.shape[1])
+    _check(_lib.lora_fused_linear_noalloc(ctypes.byref(base), None if pool is None else ctypes.byref(pool),
+                                          _ptr(seg), T, x.data_ptr(), _ld(x), _ptr(v), 0 if v is None else _ld(v),
+                                          y.data_ptr(), _ld(y), d_in, d_out, flags, _stream(stream)),
+           "lora_fused_linear_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def quantize_e4m3(x, q, s_x, stream=None) -> None:

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -301,6 +302,62 @@ int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const in
   if (T == 0 || d_out == 0) return LORA_OK;
   return hip_status(lora::launch_fused(*base, pool, const_cast<int32_t*>(seg), T, x, ld_x, v, ld_v, y, ld_y, d_in,
                                        d_out, flags, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- the allocation-free fused call ----------------------------------------
+// Device scratch of lora_fused_linear_noalloc: one copy per GPU (each device
+// that loads the library holds its own), kept until the process ends.  Host
+// code never passes this name to a kernel or a copy: it is a host-side stand-
+// in for the symbol; the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch (set-up on the first call per device).
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+int lora_fused_linear_noalloc(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
+                              const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,
+                              int32_t d_in, int32_t d_out, int32_t flags, void* stream) {
+  const int st = check_fused(base, pool, seg, T, x, ld_x, v, ld_v, y, ld_y, d_in, d_out, flags);
+  if (st != LORA_OK) return st;
+  const size_t need = lora::fused_workspace_bytes(T, d_in, d_out, base->dtype, flags, pool ? pool->r_cap : 0);
+  if (need > LORA_NOALLOC_SCRATCH_BYTES) {
+    g_last_error = "lora_fused_linear_noalloc: the call needs " + std::to_string(need) +
+                   " bytes of scratch, more than the static " + std::to_string((size_t)LORA_NOALLOC_SCRATCH_BYTES);
+    return LORA_E_SIZE;
+  }
+  if (T == 0 || d_out == 0) return LORA_OK;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int sp = hip_status(scratch_ptr(&ws));
+    if (sp != LORA_OK) return sp;
+  }
+  return hip_status(lora::launch_fused(*base, pool, const_cast<int32_t*>(seg), T, x, ld_x, v, ld_v, y, ld_y, d_in,
+                                       d_out, flags, ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t lora_fused_slices_workspace_bytes(int32_t n_slices, int32_t T, int32_t d_in, const int32_t* d_out,

@@ -318,6 +318,26 @@ size_t lora_fused_workspace_bytes_rcap(int32_t T, int32_t d_in, int32_t d_out, i
                                        int32_t r_cap);
 
 /*
+ * lora_fused_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, the same kernels
+ * and the same results as lora_fused_linear, with the scratch it needs (W8A8
+ * codes and scales, split-k partial tiles, tile counters) taken from a
+ * static device array of LORA_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends.  The call allocates and
+ * frees nothing.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and give undefined
+ * results; order them on one stream.  Whatever must start at zero is cleared
+ * by a kernel on `stream` before use.  Errors: as lora_fused_linear, and
+ * LORA_E_SIZE (text in lora_last_error) when the call needs more scratch
+ * than the array holds (lora_fused_workspace_bytes_rcap gives the need).
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (8u << 20)
+int lora_fused_linear_noalloc(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
+                              const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,
+                              int32_t d_in, int32_t d_out, int32_t flags, void* stream);
+
+/*
  * Fused linear over several output slices of one input in one launch
  * ("LoRAForge" 4: the slices of a layer's fused projections, such as q / k /
  * v or gate / up, each with its own weights and adapters).  Slice s is
