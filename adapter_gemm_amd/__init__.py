@@ -19,6 +19,7 @@ LORA_OK, LORA_E_ARG, LORA_E_ID, LORA_E_RANK, LORA_E_DTYPE, LORA_E_ALIGN, LORA_E_
 F32, BF16, FP8_E4M3 = 0, 1, 2
 LAUNCH_EXACT, LAUNCH_PERSISTENT, LAUNCH_BUCKETED, LAUNCH_FULL_BATCH = 0, 1, 2, 3
 FLAG_ACT_QUANT_E4M3 = 0x1
+FLAG_SHRINK_IN_LAUNCH = 0x2
 MAX_RANK = 128
 DEV_MAX_SLOTS = 8192
 TILE_SMALL, TILE_LARGE = 16, 64

@@ -124,7 +124,20 @@ struct FusedPlan {
   size_t part_bytes;   // fp32 partial tiles when splits + lora_split > 1
   size_t counter_bytes;  // split hand-off counters, or the persistent launch's claim counters
   bool persist;        // more tiles than CUs, no split: a workgroup per CU claims tiles
+  int xrow = 128;      // x bytes per row per k-step (64: bf16 256 x 256 tiles with a 4-slot ring)
+  size_t ovl_bytes = 0;  // in-launch shrink: its claim / done / error counters
 };
+
+// The shrink run inside a fused launch (LORA_FLAG_SHRINK_IN_LAUNCH): its
+// input x (the unquantised bf16 activations) and the rank-block geometry of
+// its items.
+struct OverlapShrink {
+  const void* x;
+  int ld_x;
+};
+// Rank-block width and blocks per row tile of single-block shrink items for
+// this pool and batch (the standalone shrink's rule for the width).
+void shrink_item_geometry(const lora_pool_t& pool, int T, int* db, int* nrb);
 
 // r_cap: the adapter pool's rank capacity, 0 without a pool
 FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap);
@@ -142,11 +155,14 @@ struct FusedSlice {
 };
 // CUs of the current device (256 if the query fails)
 int fused_device_cus();
+// Whether this plan runs the shrink inside the fused launch (the flag set,
+// 64- or 128-row tiles of bf16 or W8A16, no k split)
+bool fused_ovl_supported(const FusedPlan& pl, int base_dtype, int flags);
 // The plan of one launch over n slices (dma false: the slices go one by one).
 FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int base_dtype, int flags);
 hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, int n, const int32_t* seg, int T,
                                    const void* x, int ld_x, const float* s_x, int d_in, int flags, void* part_ws,
-                                   hipStream_t st);
+                                   hipStream_t st, const OverlapShrink* ovl = nullptr);
 hipError_t launch_fused_slices(const FusedSlice* sl, int n, int32_t* seg, int T, const void* x, int ld_x, int d_in,
                                int flags, void* workspace, hipStream_t st);
 size_t fused_slices_workspace_bytes(int T, int d_in, const int32_t* d_out, const int32_t* r_cap, int n,
@@ -156,7 +172,7 @@ bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, i
 hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,
                             const int32_t* seg, int T, const void* x, int ld_x, const float* s_x, const float* v,
                             int ld_v, void* y, int ld_y, int d_in, int d_out, int flags, void* part_ws,
-                            hipStream_t st);
+                            hipStream_t st, const OverlapShrink* ovl = nullptr);
 // bytes of the workspace for one fused call: [W8A8 codes + scales][partials][counters]
 size_t fused_quant_bytes(int T, int d_in, int flags, int base_dtype);
 size_t fused_workspace_bytes(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap);

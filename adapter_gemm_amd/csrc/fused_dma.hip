@@ -39,6 +39,7 @@
 // counter per tile) adds the partials in split order, so the result does not
 // depend on which workgroup finished last, writes y and re-arms the counter.
 #include "common.h"
+#include "shrink_core.h"
 
 #include <algorithm>
 
@@ -91,7 +92,16 @@ struct DmaArgs {
   int n_work;             // work items: tiles x (splits + lora_split)
   int n_slices;           // > 1: the per-slice fields above come from sl[]
   SliceArgs sl[kMaxSlices];
+  // in-launch shrink (n_prod > 0): the first n_prod workgroups take shrink
+  // items from a claim counter; tiles help with any left when their main loop
+  // ends and wait until all are done before they read v
+  int n_prod;
+  int32_t* ovc;           // {claimed, done, error}, cleared before the launch
+  ShrinkArgs sh;
 };
+
+constexpr int kSc1 = 16;                    // cache-policy bits of a device-coherent (sc1) buffer access
+constexpr long kOvlSpinLimit = 1L << 22;    // bound of a tile's wait for the in-launch shrink (seconds)
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -176,6 +186,20 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* sums, int* total)
 
 __device__ __forceinline__ int sw128(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 __device__ __forceinline__ int sw64(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+// 16-byte chunk c of an LDS row of RB bytes (128 or 64), XOR-swizzled so that
+// the 16 rows of a fragment read spread over the LDS banks
+template <int RB>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (RB == 128) return sw128(row, c);
+  else return sw64(row, c);
+}
+// inverse of the swizzle for the DMA: the chunk whose data lands at physical
+// chunk position cl of row `row`
+template <int RB>
+__device__ __forceinline__ int swz_src(int row, int cl) {
+  if constexpr (RB == 128) return cl ^ (row & 7);
+  else return cl ^ ((row >> 2) & 3);
+}
 
 // 8 e4m3 codes -> 8 bf16, exact (e4m3 values have 4 significant bits)
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 c) {
@@ -191,13 +215,17 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 c) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN, bool PERSIST>
+template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN, bool PERSIST, int XROW = 128, bool OVL = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   constexpr int NW = WGM * WGN, NT = 64 * NW;          // waves (WGM x WGN grid) and threads
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int WROW = MODE == kW8A16 ? 64 : 128;      // W bytes per row per k-step
-  constexpr int XS = BM * 128, WSB = BN * WROW, STAGE = XS + WSB;
+  // x bytes per row per k-step (XROW: 128, or 64 for the bf16 ring of
+  // shorter, more numerous steps) and W bytes (fp8 codes: half as many)
+  static_assert(XROW == 128 || (XROW == 64 && MODE == kBF16), "64-byte k-steps: bf16 only");
+  constexpr int WROW = MODE == kW8A16 ? 64 : XROW;
+  constexpr int KK = XROW / 64;                        // 32-wide k chunks per step (bf16, W8A16)
+  constexpr int XS = BM * XROW, WSB = BN * WROW, STAGE = XS + WSB;
   constexpr int LX = XS / (1024 * NW), LW = WSB / (1024 * NW), L = LX + LW;   // DMA ops per wave per step
   constexpr int RING = STAGES * STAGE;
   constexpr int BSLICE = BN * 128;                     // one adapter step: BN channels x 64 packed ranks
@@ -233,6 +261,66 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // CU that claims the next item of its XCD from a counter until none is
   // left: a CU that finishes early takes more items, where the hardware would
   // otherwise hold a ready CU idle behind a busy one.
+  // In-launch shrink ("EpiLoRA" 3.1, the decode path: the down-projection
+  // runs while the GEMM streams its weights, and the epilogue needs its
+  // result only at the end).  Items are claimed from ovc[0]; the workgroup
+  // that claims one runs it, stores v device-coherently, and counts it done
+  // in ovc[1].  Every claimed item is run by a workgroup that is already
+  // running, so the count reaches the total whatever the hardware schedules.
+  auto ovl_items = [&](bool wait) {
+    const SegPtrs SP = seg_ptrs(const_cast<int32_t*>(a.seg), a.T);
+    const bool valid = SP.sum[kError] == 0 && SP.sum[kRows] == a.T;
+    // every value that steers the loop below is made wave-uniform for the
+    // compiler: a branch it takes for divergent would put the loop's
+    // barriers under divergent control flow
+    const int n_items = __builtin_amdgcn_readfirstlane(valid ? SP.sum[kNTilesSmall] * a.sh.nrb : 0);
+    f32x4_t (*red)[64] = reinterpret_cast<f32x4_t (*)[64]>(ring);
+    lds_barrier();                              // the ring is free (every wave is past its LDS reads)
+    // one lane-0 region per iteration, at its top: count the item the
+    // workgroup finished last (its v stores drained by the barrier below
+    // it), then claim the next
+    int counted = 1;
+    for (;;) {
+      if (threadIdx.x == 0) {
+        if (!counted) __hip_atomic_fetch_add(&a.ovc[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_claim = __hip_atomic_fetch_add(&a.ovc[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      lds_barrier();
+      const int k = __builtin_amdgcn_readfirstlane(s_claim);
+      lds_barrier();
+      if (k >= n_items) break;
+      const int ti = k / a.sh.nrb, rb = k - ti * a.sh.nrb;
+      TileWork w;
+      w.p0 = __builtin_amdgcn_readfirstlane(SP.tiles_small[2 * ti]);
+      w.seg = __builtin_amdgcn_readfirstlane(SP.tiles_small[2 * ti + 1]);
+      w.rows = 0;
+      shrink_item_body<uint16_t, 1, NW, true>(a.sh, SP, w, rb, red);
+      vm_barrier<0>();                          // every wave's v stores have completed
+      counted = 0;
+    }
+    if (wait) {
+      if (threadIdx.x == 0) {
+        long spins = 0;
+        while (__hip_atomic_load(&a.ovc[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_items) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kOvlSpinLimit) {        // never expected: report instead of hanging
+            __hip_atomic_store(&a.ovc[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      }
+      lds_barrier();
+    }
+  };
+  int bid = (int)blockIdx.x;
+  if constexpr (OVL) {
+    if (bid < a.n_prod) {
+      ovl_items(false);
+      return;
+    }
+    bid -= a.n_prod;                            // (n_prod is a multiple of 8: bid & 7 is still the XCD)
+  }
+
   const int S_total = a.splits + a.lora_split;
   const int full = (a.n_work / 8) * 8, per_xcd = full / 8, xcd = blockIdx.x & 7;
   // (persistent) a workgroup claims its next item only once it is free:
@@ -244,13 +332,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     if (round > 0) lds_barrier();               // every wave is past the last tile's LDS reads
     if (tid == 0) s_claim = __hip_atomic_fetch_add(&a.counters[xcd], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();
-    const int k = s_claim;
+    const int k = __builtin_amdgcn_readfirstlane(s_claim);   // wave-uniform: the loop holds barriers
     if (k < per_xcd) pid = xcd * per_xcd + k;
     else if (k == per_xcd && full + xcd < a.n_work) pid = full + xcd;
     else break;
   } else {
     if (round > 0) break;
-    pid = blockIdx.x;
+    pid = bid;
     if (pid < full) pid = (pid & 7) * per_xcd + (pid >> 3);
   }
   const int tile = pid / S_total, split = pid - tile * S_total;
@@ -394,7 +482,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           bq[q][j][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bqr, (int)o, h * 16, 0));
       }
     }
-    if (row_epi && m0 < min(m0 + BM, n_active)) {
+    if (row_epi && m0 < min(m0 + BM, n_active) && !OVL) {
       // raw fp32 v rows [m0, min(m0 + BM, n_active)) x r_cap (rows past it: zeros)
       const int pe = min(m0 + BM, n_active);
       const int rq = a.r_cap / 4;
@@ -413,7 +501,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
   for (int q = 0; q < LX; ++q) {
     const int s = (wave * LX + q) * 64 + lane;
-    const int row = s >> 3, c = (s & 7) ^ (row & 7);
+    const int row = s / (XROW / 16), c = swz_src<XROW>(row, s % (XROW / 16));
     const int pos = m0 + row;
     uint32_t o = kOOB;
     if (pos < a.T) o = (uint32_t)((has_seg ? perm_q[q] : pos) * a.ld_x * XE + c * 16);
@@ -423,20 +511,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   for (int q = 0; q < LW; ++q) {
     const int s = (wave * LW + q) * 64 + lane;
     int row, c;
-    if constexpr (WROW == 128) { row = s >> 3; c = (s & 7) ^ (row & 7); }
-    else { row = s >> 2; c = (s & 3) ^ ((row >> 2) & 3); }
+    row = s / (WROW / 16);
+    c = swz_src<WROW>(row, s % (WROW / 16));
     const int n = n0 + row;
     woff[q] = n < a.d_out ? (uint32_t)(n * a.ld_w * WE + c * 16) : kOOB;
   }
   const i32x4_t xrs = rsrc(a.x, a.x_bytes);
   const i32x4_t wrs = rsrc(a.W, a.w_bytes);
 
-  auto issue = [&](int kt, int slot) {
+  // DMA operation q (0 .. L-1) of step kt into ring slot `slot`
+  auto issue_part = [&](int kt, int slot, int q) {
     uint8_t* st = ring + slot * STAGE;
+    if (q < LX) dma16(xrs, st + (wave * LX + q) * 1024, xoff[q], (uint32_t)kt * XROW);
+    else dma16(wrs, st + XS + (wave * LW + (q - LX)) * 1024, woff[q - LX], (uint32_t)kt * WROW);
+  };
+  auto issue = [&](int kt, int slot) {
 #pragma unroll
-    for (int q = 0; q < LX; ++q) dma16(xrs, st + (wave * LX + q) * 1024, xoff[q], (uint32_t)kt * 128u);
-#pragma unroll
-    for (int q = 0; q < LW; ++q) dma16(wrs, st + XS + (wave * LW + q) * 1024, woff[q], (uint32_t)kt * WROW);
+    for (int q = 0; q < L; ++q) issue_part(kt, slot, q);
   };
 
   f32x4_t acc[TM][TN];
@@ -445,7 +536,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int slot) {
+  // bf16: the next step's DMA operations go out one per row fragment between
+  // the MFMA blocks (kt_next < 0: none), so that a wave never stalls on a
+  // burst of vector-memory issues while its matrix core could be busy
+  // DMA operations per fragment block: a 2-slot ring gives the next step's
+  // loads one step to land, so they all go out in the first half of it
+  constexpr int DPB = STAGES == 2 ? 2 : 1;
+  auto compute = [&](int slot, int kt_next, int slot_next) {
     const uint8_t* As = ring + slot * STAGE;
     const uint8_t* Ws = As + XS;
     if constexpr (MODE == kW8A8) {
@@ -503,24 +600,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
         bf16x8_t fa[TM], fb[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int row = wm * WM + i * 16 + frow;
-          fa[i] = *reinterpret_cast<const bf16x8_t*>(As + sw128(row, kk * 4 + fk));
+          fa[i] = *reinterpret_cast<const bf16x8_t*>(As + swz<XROW>(row, kk * 4 + fk));
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int row = wn * WN + j * 16 + frow;
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(Ws + sw128(row, kk * 4 + fk));
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(Ws + swz<XROW>(row, kk * 4 + fk));
         }
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int u = 0; u < DPB; ++u) {
+            const int q = (kk * TM + i) * DPB + u;
+            if (kt_next >= 0 && q < L) issue_part(kt_next, slot_next, q);
+          }
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
       }
+#pragma unroll
+      for (int q = KK * TM * DPB; q < L; ++q)
+        if (kt_next >= 0) issue_part(kt_next, slot_next, q);
     }
   };
 
@@ -530,8 +636,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     if (p < nsteps) issue(kbeg + p, p);
   for (int t = 0; t < nsteps; ++t) {
     wait_step<L, STAGES - 2>(min(STAGES - 2, nsteps - 1 - t));
-    if (t + STAGES - 1 < nsteps) issue(kbeg + t + STAGES - 1, (t + STAGES - 1) % STAGES);
-    compute(t % STAGES);
+    const bool more = t + STAGES - 1 < nsteps;
+    if constexpr (MODE == kBF16) {
+      compute(t % STAGES, more ? kbeg + t + STAGES - 1 : -1, (t + STAGES - 1) % STAGES);
+    } else {
+      if (more) issue(kbeg + t + STAGES - 1, (t + STAGES - 1) % STAGES);
+      compute(t % STAGES, -1, 0);
+    }
   }
 
   const int row_base = m0 + wm * WM;   // first grouped position of this wave's rows
@@ -561,6 +672,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     }
   }
 
+  // in-launch shrink: help with the items still unclaimed, then wait for all
+  // of them before any read of v
+  if constexpr (OVL)
+    if (do_lora) ovl_items(true);
+
   // ---- adapter phase, per output (decode tiles, ranks <= 16) ------------------
   // Each lane adds, to every output it holds, s_a sum_j v[row, j] B_a[n, j]
   // of its row's adapter in fp32 ("LoRAForge" 5, RowExpand: a channel's rank
@@ -570,8 +686,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // holds up to ~25 groups of rank 16.
   if constexpr (kRowEpi) {
     if (row_epi && m0 < min(m0 + BM, n_active)) {
-      vm_barrier<0>();                          // every wave's v rows and B rows have landed
       const int rq = a.r_cap / 4;
+      if constexpr (OVL) {
+        // v of this launch: device-coherent loads (the raw v rows, rows past
+        // the live ones as zeros), then into LDS
+        const int pe = min(m0 + BM, n_active);
+        const __amdgpu_buffer_rsrc_t vr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.v), 0, (int)a.v_bytes, kBufferWord3);
+        for (int c = tid; c < BM * rq; c += NT) {
+          const int row = c / rq, c4 = c - row * rq;
+          u32x4_t val = {0, 0, 0, 0};
+          if (m0 + row < pe)
+            val = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  vr, ((m0 + row) * a.ld_v + c4 * 4) * 4, 0, kSc1));
+          *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(v_rows) + c * 16) = val;
+        }
+      }
+      vm_barrier<0>();                          // every wave's v rows and B rows have landed
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -642,7 +773,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
         const int row = c / rq, phys = c - row * rq;
         const int c4 = (phys + rq - (row / vd) % rq) % rq;
         const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
-        dma16(vrs, bsl + c0 * 16, o, 0u);
+        if constexpr (!OVL) {
+          dma16(vrs, bsl + c0 * 16, o, 0u);
+        } else {
+          // v of this launch: a device-coherent load into registers, then LDS
+          const __amdgpu_buffer_rsrc_t vr =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.v), 0, (int)a.v_bytes, kBufferWord3);
+          u32x4_t val = {0, 0, 0, 0};
+          if (o != kOOB) val = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)o, 0, kSc1));
+          *reinterpret_cast<u32x4_t*>(bsl + c * 16) = val;
+        }
       }
       // group table (segments meeting the tile's live rows)
       if (tid < BM) t_rowseg[tid] = my_rowseg;
@@ -810,7 +950,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     // drains its stores (vmcnt(0)) before the barrier that precedes the
     // counter increment, and the reads are issued only after the increment
     // that found all other partials counted.
-    constexpr int kSc1 = 16;                     // cache-policy bits: sc1
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, 0x7fffffff, kBufferWord3);
     const uint32_t wave_off = (uint32_t)(wave * TM * TN * 256) * 4u;
 #pragma unroll
@@ -881,22 +1020,26 @@ int resident_per_cu(K kernel, int threads) {
   return n;
 }
 
-template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN, bool PERSIST = false>
+template <int BM, int BN, int MODE, int STAGES, int WGM, int WGN, bool PERSIST = false, int XROW = 128,
+          bool OVL = false>
 hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
   const int S_total = a.splits + a.lora_split;
-  if (S_total > 1 || pl.persist) {
-    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, a.counters,
-                       pl.persist ? kPersistCounters : pl.tiles);
+  // counters (split hand-off or persistent claims), then the in-launch
+  // shrink's, contiguous: one clearing kernel for all
+  const int n_counters = (int)(pl.counter_bytes / sizeof(int32_t)) + (a.n_prod > 0 ? 4 : 0);
+  if (n_counters > 0) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, a.counters, n_counters);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  auto kernel = fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN, PERSIST>;
+  auto kernel = fused_dma_kernel<BM, BN, MODE, STAGES, WGM, WGN, PERSIST, XROW, OVL>;
   int grid = a.n_work;
   if (PERSIST) {
     // as many persistent workgroups as the chip holds at once
     static const int per_cu = resident_per_cu(kernel, 64 * WGM * WGN);
     grid = std::min(a.n_work, device_cus() * per_cu);
   }
+  if constexpr (OVL) grid += a.n_prod;         // shrink producers at the head of the grid
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * WGM * WGN), 0, st, a);
   return hipGetLastError();
 }
@@ -904,7 +1047,9 @@ hipError_t launch_cfg(DmaArgs a, const FusedPlan& pl, hipStream_t st) {
 template <int MODE>
 hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
   if constexpr (MODE == kBF16)
-    if (pl.bm == 256 && pl.bn == 256) return launch_cfg<256, 256, MODE, 2, 4, 2>(a, pl, st);
+    if (pl.bm == 256 && pl.bn == 256)
+      return pl.xrow == 64 ? launch_cfg<256, 256, MODE, 4, 4, 2, false, 64>(a, pl, st)
+                           : launch_cfg<256, 256, MODE, 2, 4, 2>(a, pl, st);
   if constexpr (MODE != kW8A16)
     if (pl.bm == 256) return launch_cfg<256, 128, MODE, 3, 4, 2>(a, pl, st);
   // 8 waves (two per SIMD) hide LDS and barrier latency; the wave grids are
@@ -914,15 +1059,32 @@ hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
   // reads and code widening overlap the other's MFMAs (measured: fp8
   // 8192 -> 28672, 512 rows, 500 -> 418 us against one 8-wave workgroup).
   // (64- and 128-row tiles: persistent above one tile per CU)
+  // (the in-launch shrink: 64- and 128-row tiles of bf16 and W8A16 only)
   if constexpr (MODE == kW8A16) {
-    if (pl.bm == 128)
+    if (pl.bm == 128) {
+      if (a.n_prod > 0)
+        return pl.persist ? launch_cfg<128, 128, MODE, 3, 2, 2, true, 128, true>(a, pl, st)
+                          : launch_cfg<128, 128, MODE, 3, 2, 2, false, 128, true>(a, pl, st);
       return pl.persist ? launch_cfg<128, 128, MODE, 3, 2, 2, true>(a, pl, st)
                         : launch_cfg<128, 128, MODE, 3, 2, 2>(a, pl, st);
+    }
+    if (a.n_prod > 0)
+      return pl.persist ? launch_cfg<64, 64, MODE, 4, 2, 2, true, 128, true>(a, pl, st)
+                        : launch_cfg<64, 64, MODE, 4, 2, 2, false, 128, true>(a, pl, st);
     return pl.persist ? launch_cfg<64, 64, MODE, 4, 2, 2, true>(a, pl, st) : launch_cfg<64, 64, MODE, 4, 2, 2>(a, pl, st);
   } else {
-    if (pl.bm == 128)
+    if (pl.bm == 128) {
+      if constexpr (MODE == kBF16)
+        if (a.n_prod > 0)
+          return pl.persist ? launch_cfg<128, 128, MODE, 4, 4, 2, true, 128, true>(a, pl, st)
+                            : launch_cfg<128, 128, MODE, 4, 4, 2, false, 128, true>(a, pl, st);
       return pl.persist ? launch_cfg<128, 128, MODE, 4, 4, 2, true>(a, pl, st)
                         : launch_cfg<128, 128, MODE, 4, 4, 2>(a, pl, st);
+    }
+    if constexpr (MODE == kBF16)
+      if (a.n_prod > 0)
+        return pl.persist ? launch_cfg<64, 64, MODE, 4, 4, 2, true, 128, true>(a, pl, st)
+                          : launch_cfg<64, 64, MODE, 4, 4, 2, false, 128, true>(a, pl, st);
     return pl.persist ? launch_cfg<64, 64, MODE, 4, 4, 2, true>(a, pl, st) : launch_cfg<64, 64, MODE, 4, 4, 2>(a, pl, st);
   }
 }
@@ -932,17 +1094,24 @@ hipError_t launch_mode(const DmaArgs& a, const FusedPlan& pl, hipStream_t st) {
 namespace {
 // LDS ring of one configuration, and whether the adapter phase (fp32 v rows,
 // the packed chunk map and at least two B slices) fits in it.
-int ring_bytes(int bm, int bn, bool w8a16, int stages) { return stages * (bm * 128 + bn * (w8a16 ? 64 : 128)); }
-bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap) {
+int ring_bytes(int bm, int bn, bool w8a16, int stages, int xrow = 128) {
+  return stages * (bm * xrow + bn * (w8a16 ? xrow / 2 : xrow));
+}
+bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap, int xrow = 128) {
   if (r_cap <= 0) return true;
   const int cap_chunks = bm * r_cap / 8;
   const int used = (bm * r_cap * 2 + cap_chunks * 8 + (cap_chunks / 4 + 1) * 4 + 1023) & ~1023;
-  const int avail = ring_bytes(bm, bn, w8a16, stages) - used;
+  const int avail = ring_bytes(bm, bn, w8a16, stages, xrow) - used;
   return avail >= 2 * bn * 128 && avail >= bm * r_cap * 4;   // two B slices; the raw v rows
 }
 }  // namespace
 
 int fused_device_cus() { return device_cus(); }
+
+bool fused_ovl_supported(const FusedPlan& pl, int base_dtype, int flags) {
+  return (flags & LORA_FLAG_SHRINK_IN_LAUNCH) && pl.dma && pl.bm <= 128 && pl.splits == 1 && pl.lora_split == 0 &&
+         (base_dtype == LORA_BF16 || (base_dtype == LORA_FP8_E4M3 && !(flags & LORA_FLAG_ACT_QUANT_E4M3)));
+}
 
 FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap) {
   FusedPlan pl{};
@@ -956,8 +1125,10 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   // the largest tile that still gives every CU a tile (>= 256 tiles), else
   // 64 x 64; 256-row tiles are not built for the widened-fp8 mode
   // (256 x 256 needs two full rounds of the chip to beat 256 x 128's balance)
-  struct Cfg { int bm, bn, stages, min_tiles; };
-  const Cfg cands[] = {{256, 256, 2, 512}, {256, 128, 3, 256}, {128, 128, 4, 256}, {64, 64, 4, 0}};
+  // (bf16 256 x 256: xrow = 64 would be a 4-slot ring of 64-byte k-steps)
+  struct Cfg { int bm, bn, stages, min_tiles, xrow; };
+  const Cfg cands[] = {{256, 256, 2, 512, 128}, {256, 128, 3, 256, 128}, {128, 128, 4, 256, 128},
+                       {64, 64, 4, 0, 128}};
   auto tiles_of = [&](const Cfg& c) { return (long)((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn); };
   const Cfg* pick = nullptr;
   for (const Cfg& c : cands) {
@@ -967,7 +1138,7 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
     if (c.bm == 256 && c.bn == 256 && w8a8) continue;
     // ring slots as launched (W8A16 128 x 128: 3, two workgroups per CU)
     const int stages = (w8a16 && c.bm == 128) ? 3 : c.stages;
-    if (!lora_fits(c.bm, c.bn, w8a16, stages, r_cap)) continue;
+    if (!lora_fits(c.bm, c.bn, w8a16, stages, r_cap, c.xrow)) continue;
     if (tiles_of(c) >= c.min_tiles) { pick = &c; break; }
   }
   // 256 x 128 against 256 x 256 when the output fills the chip with the
@@ -975,7 +1146,8 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   // measured cost of one tile (bf16, 4096-deep: 256 x 256 ~114 us, 256 x 128
   // ~72 us on MI355X), so that 1.5 rounds of the smaller tile do not beat a
   // part-filled round of the larger one
-  if (pick && pick->bm == 256 && pick->bn == 128 && !w8a8 && lora_fits(256, 256, w8a16, cands[0].stages, r_cap)) {
+  if (pick && pick->bm == 256 && pick->bn == 128 && !w8a8 &&
+      lora_fits(256, 256, w8a16, cands[0].stages, r_cap, cands[0].xrow)) {
     const long cus = device_cus();
     const long r256 = (tiles_of(cands[0]) + cus - 1) / cus, r128 = (tiles_of(*pick) + cus - 1) / cus;
     if (r256 * 114 < r128 * 72) pick = &cands[0];
@@ -984,14 +1156,16 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   pl.dma = true;
   pl.bm = pick->bm;
   pl.bn = pick->bn;
-  pl.nk = d_in / kb;
+  pl.xrow = (w8a8 || w8a16) ? 128 : pick->xrow;
+  pl.nk = d_in / (w8a8 ? kb : pl.xrow / 2);
   pl.tiles_m = (T + pl.bm - 1) / pl.bm;
   pl.tiles_n = (d_out + pl.bn - 1) / pl.bn;
   pl.tiles = pl.tiles_m * pl.tiles_n;
   // very small outputs: split k over up to 4 workgroups per tile (at least 8
   // k-steps each), plus one for the adapter phase
   pl.splits = 1;
-  if (pl.tiles < 64) pl.splits = std::max(1, std::min(4, pl.nk / 8));
+  // (no k split with the in-launch shrink: its producers fill the chip)
+  if (pl.tiles < 64 && !(flags & LORA_FLAG_SHRINK_IN_LAUNCH)) pl.splits = std::max(1, std::min(4, pl.nk / 8));
   pl.lora_split = (pl.splits > 1 && r_cap > 0) ? 1 : 0;
   const int S_total = pl.splits + pl.lora_split;
   // persistent: 64- and 128-row tiles with more tiles than CUs (measured:
@@ -1000,6 +1174,7 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   pl.part_bytes = S_total > 1 ? (size_t)pl.tiles * S_total * pl.bm * pl.bn * sizeof(float) : 0;
   pl.counter_bytes = S_total > 1 ? (size_t)pl.tiles * sizeof(int32_t)
                                  : (pl.persist ? kPersistCounters * sizeof(int32_t) : 0);
+  pl.ovl_bytes = fused_ovl_supported(pl, base_dtype, flags) && r_cap > 0 ? 64 : 0;
   return pl;
 }
 
@@ -1011,7 +1186,8 @@ size_t fused_quant_bytes(int T, int d_in, int flags, int base_dtype) {
 
 size_t fused_workspace_bytes(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap) {
   const FusedPlan pl = plan_fused(T, d_in, d_out, base_dtype, flags, r_cap);
-  return fused_quant_bytes(T, d_in, flags, base_dtype) + (pl.dma ? pl.part_bytes + pl.counter_bytes : 0);
+  return fused_quant_bytes(T, d_in, flags, base_dtype) +
+         (pl.dma ? pl.part_bytes + pl.counter_bytes + pl.ovl_bytes : 0);
 }
 
 bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, int base_dtype, int flags,
@@ -1049,7 +1225,7 @@ FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int ba
 
 hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, int n, const int32_t* seg, int T,
                                    const void* x, int ld_x, const float* s_x, int d_in, int flags, void* part_ws,
-                                   hipStream_t st) {
+                                   hipStream_t st, const OverlapShrink* ovl) {
   const lora_base_t& base = sl[0].base;
   const bool w8a8 = base.dtype == LORA_FP8_E4M3 && (flags & LORA_FLAG_ACT_QUANT_E4M3);
   const int wel = base.dtype == LORA_BF16 ? 2 : 1;
@@ -1112,6 +1288,32 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
   a.lora_split = sl[0].pool ? pl.lora_split : 0;
   a.n_work = pl.tiles * (a.splits + a.lora_split);
   a.n_slices = n > 1 ? n : 1;
+  a.n_prod = 0;
+  a.ovc = a.counters + pl.counter_bytes / sizeof(int32_t);
+  if (ovl && sl[0].pool && n == 1 && fused_ovl_supported(pl, base.dtype, flags)) {
+    // the in-launch shrink over the pool of the (single) slice
+    const lora_pool_t& pool = *sl[0].pool;
+    ShrinkArgs& sh = a.sh;
+    sh.x = ovl->x;
+    sh.A = pool.A;
+    sh.slot_rank = pool.slot_rank;
+    sh.seg = const_cast<int32_t*>(seg);
+    sh.v = const_cast<float*>(sl[0].v);
+    sh.ld_x = ovl->ld_x;
+    sh.r_cap = pool.r_cap;
+    sh.d_in = pool.d_in;
+    sh.T = T;
+    sh.ld_v = sl[0].ld_v;
+    sh.mode = LORA_LAUNCH_PERSISTENT;
+    shrink_item_geometry(pool, T, &sh.db, &sh.nrb);
+    sh.rtiles = 0;
+    sh.n_items = 0;
+    sh.slots = std::min(T, pool.n_slots);
+    // producers: about one workgroup per 4 items of the bound, at most 64, a
+    // multiple of 8 (a tile's workgroup index keeps its XCD)
+    const long bound = ((long)T / LORA_TILE_SMALL + sh.slots) * sh.nrb;
+    a.n_prod = (int)std::min<long>(64, std::max<long>(8, (bound / 4 + 7) / 8 * 8));
+  }
   if (n > 1) {
     int tn0 = 0;
     for (int s = 0; s < n; ++s) {
@@ -1128,9 +1330,9 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
 hipError_t launch_fused_dma(const FusedPlan& pl, const lora_base_t& base, const lora_pool_t* pool,
                             const int32_t* seg, int T, const void* x, int ld_x, const float* s_x, const float* v,
                             int ld_v, void* y, int ld_y, int d_in, int d_out, int flags, void* part_ws,
-                            hipStream_t st) {
+                            hipStream_t st, const OverlapShrink* ovl) {
   const FusedSlice one{base, pool, v, ld_v, y, ld_y, d_out};
-  return launch_fused_dma_slices(pl, &one, 1, seg, T, x, ld_x, s_x, d_in, flags, part_ws, st);
+  return launch_fused_dma_slices(pl, &one, 1, seg, T, x, ld_x, s_x, d_in, flags, part_ws, st, ovl);
 }
 
 }  // namespace lora

@@ -543,7 +543,20 @@ hipError_t launch_fused(const lora_base_t& base, const lora_pool_t* pool, int32_
     xin = q;
     ld_in = ld_q;
   }
-  if (fused_dma_fits(pl, T, ld_in, d_out, base.ld_w, base.dtype, flags, pool))
+  const bool in_launch = (flags & LORA_FLAG_SHRINK_IN_LAUNCH) && pool;
+  const bool dma = fused_dma_fits(pl, T, ld_in, d_out, base.ld_w, base.dtype, flags, pool);
+  if (dma && in_launch && fused_ovl_supported(pl, base.dtype, flags)) {
+    const OverlapShrink ovl{x, ld_x};
+    return launch_fused_dma(pl, base, pool, seg, T, xin, ld_in, s_x, v, ld_v, y, ld_y, d_in, d_out, flags,
+                            static_cast<uint8_t*>(workspace) + qbytes, st, &ovl);
+  }
+  if (in_launch) {
+    // shapes the pipelined kernel does not take: the shrink as its own launch first
+    LaunchShape ls{LORA_LAUNCH_PERSISTENT, 0, 0, std::min(T, pool->n_slots)};
+    hipError_t e = launch_shrink(*pool, seg, T, ls, x, ld_x, const_cast<float*>(v), ld_v, st);
+    if (e != hipSuccess) return e;
+  }
+  if (dma)
     return launch_fused_dma(pl, base, pool, seg, T, xin, ld_in, s_x, v, ld_v, y, ld_y, d_in, d_out, flags,
                             static_cast<uint8_t*>(workspace) + qbytes, st);
   a.x = xin;

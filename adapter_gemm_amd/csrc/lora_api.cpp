@@ -258,12 +258,16 @@ int check_fused(const lora_base_t* base, const lora_pool_t* pool, const int32_t*
                 int32_t flags) {
   if (!base || !base->W) return LORA_E_ARG;
   if (T < 0 || d_in < 0 || d_out < 0 || (T > 0 && (!x || !y))) return LORA_E_ARG;
-  if (flags & ~LORA_FLAG_ACT_QUANT_E4M3) return LORA_E_ARG;
+  if (flags & ~(LORA_FLAG_ACT_QUANT_E4M3 | LORA_FLAG_SHRINK_IN_LAUNCH)) return LORA_E_ARG;
   const int bt = base->dtype;
   if (bt != LORA_F32 && bt != LORA_BF16 && bt != LORA_FP8_E4M3) return LORA_E_DTYPE;
   const int dt = bt == LORA_F32 ? LORA_F32 : LORA_BF16;   // x, pool and y type
   if (bt == LORA_FP8_E4M3 && !base->w_scale) return LORA_E_ARG;
   if ((flags & LORA_FLAG_ACT_QUANT_E4M3) && bt != LORA_FP8_E4M3) return LORA_E_DTYPE;
+  if (flags & LORA_FLAG_SHRINK_IN_LAUNCH) {        // v is computed by the call from x
+    if (!pool) return LORA_E_ARG;
+    if (bt == LORA_F32) return LORA_E_DTYPE;
+  }
   if (pool) {
     int st = check_pool(pool);
     if (st != LORA_OK) return st;
@@ -382,6 +386,7 @@ int lora_fused_linear_slices(int32_t n_slices, const lora_base_t* bases, const l
                              const int32_t* ld_y, int32_t flags, void* workspace, size_t workspace_bytes,
                              void* stream) {
   if (n_slices < 1 || !bases || !d_out || !y || !ld_y || ((pools != nullptr) != (v != nullptr))) return LORA_E_ARG;
+  if (flags & LORA_FLAG_SHRINK_IN_LAUNCH) return LORA_E_ARG;   // (single-projection calls only)
   if (pools && !ld_v) return LORA_E_ARG;
   std::vector<lora::FusedSlice> sl(n_slices);
   std::vector<int32_t> rc(n_slices, 0);

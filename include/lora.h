@@ -120,6 +120,8 @@ enum {
 /* ---- fused-linear flags ---------------------------------------------- */
 #define LORA_FLAG_ACT_QUANT_E4M3 0x1  /* fp8 base: quantise x per token
                                          (W8A8); default is W8A16           */
+#define LORA_FLAG_SHRINK_IN_LAUNCH 0x2 /* lora_fused_linear computes v itself,
+                                         in the same launch (see there)     */
 
 /* Adapter pool of one projection (device pointers). */
 typedef struct {
@@ -300,6 +302,20 @@ int lora_expand(const lora_pool_t* pool, const int32_t* seg, int32_t T, const lo
  *            LORA_E_SIZE if it is missing or too small.
  * y must not alias x.  Results do not depend on the schedule's timing: split
  * partial tiles are added in a fixed order.
+ *
+ * LORA_FLAG_SHRINK_IN_LAUNCH ("EpiLoRA" 3.1, the decode path and Fig. 1c: the
+ * down-projection runs while the GEMM streams its weights, and only the
+ * epilogue needs its result): v becomes an output, v = A_a x for the live
+ * rows, computed in the same launch as the product.  The first workgroups of
+ * the grid take shrink items (a row tile of one segment and a block of rank
+ * directions, as lora_shrink's) from a counter in the workspace; a tile that
+ * reaches its epilogue first runs any items still unclaimed, then waits until
+ * every item is done and reads v, so progress never depends on which
+ * workgroups the hardware schedules.  Needs a pool and a bf16 or fp8 base
+ * (not fp32); the shrink reads the unquantised x (W8A8 included).  v equals
+ * lora_shrink's up to fp32 rounding (the k chunks are added in another fixed
+ * order) and is deterministic.  Shapes the pipelined kernel does not take run
+ * lora_shrink and then the fused product, two launches, with the same result.
  */
 int lora_fused_linear(const lora_base_t* base, const lora_pool_t* pool, const int32_t* seg, int32_t T,
                       const void* x, int32_t ld_x, const float* v, int32_t ld_v, void* y, int32_t ld_y,

@@ -431,6 +431,75 @@ def test_fused_pipelined_parity(case):
             assert rel_l2(y8, ref8) <= TOL["bf16"] and row_rel_l2(y8, ref8) <= TOL["bf16"]
 
 
+# ---- the shrink inside the fused launch (LORA_FLAG_SHRINK_IN_LAUNCH) ----------
+
+# decode-sized tiles run the shrink in the same launch (64x64 bf16 one-shot and
+# persistent, 128x128 bf16 persistent, W8A16 64x64 and 128x128 persistent);
+# other plans (256-row tiles, W8A8) run it as a launch of its own first
+INLAUNCH = {
+    "decode_64": ("decode_bgmv", dict(T=300, d_in=1024, d_out=1048, n_slots=40)),
+    "decode_small_split_shape": ("decode_bgmv", dict(T=100, d_in=1024, d_out=264, n_slots=40)),
+    "decode_persistent": ("decode_bgmv", dict(T=600, d_in=1024, d_out=3000, n_slots=40)),
+    "prefill_persistent128": ("prefill_sgmv", dict(T=1100, d_in=512, d_out=4104, n_slots=24, n_req=5)),
+    "fp8_persistent64": ("fp8_fused", dict(T=520, d_in=512, d_out=4112, n_slots=32, r=64)),
+    "fp8_wide128": ("fp8_fused", dict(T=600, d_in=256, d_out=16376, n_slots=32, r=64)),
+    "prefill_256_fallback": ("prefill_sgmv", dict(T=2000, d_in=512, d_out=4088, n_slots=24, n_req=9)),
+    "released_rows": ("llama_layer", dict(n_slots=96, n_req=3, prefill_len=40, n_decode=70,
+                                          shapes=[("q", 1024, 1048)])),
+}
+
+
+def _fused_in_launch(dp, seg, w, flags=0):
+    p = dp.p
+    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)     # an output of the call
+    y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(dp.ydtype)
+    bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3}[p.base_dtype]
+    f = flags | agm.FLAG_SHRINK_IN_LAUNCH
+    ws = agm.fused_workspace(w.T, p.d_in, p.d_out, bt, f, device=DEV)
+    agm.fused_linear(dp.base, dp.pool, seg, dp.x, v, y, flags=f, workspace=ws)
+    torch.cuda.synchronize()
+    return to_f64(y), v.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("case", list(INLAUNCH))
+def test_fused_shrink_in_launch_parity(case):
+    """EpiLoRA's decode path: the fused call computes v itself, in the same
+    launch; v and y against the fp64 oracle, inactive rows against the base
+    alone, and two calls bitwise equal."""
+    name, kw = INLAUNCH[case]
+    w = make_workload(name, **kw)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, p.n_slots)
+    print(f"case {case}: T={w.T} {p.d_in}->{p.d_out} r_cap={p.r_cap}", flush=True)
+    y, v = _fused_in_launch(dp, seg, w)
+    segd = split_seg(seg, w.T)
+    n = s.n_active
+    v_ref = _v_ref(dp, w, segd)
+    rk = p.slot_rank[segd["seg_adapter"][segd["pos_seg"][:n]]] if n else np.zeros(0, int)
+    mask = np.arange(p.r_cap)[None, :] < rk[:, None]
+    assert rel_l2(v[:n][mask], v_ref[mask]) <= TOL["fp32"], (case, rel_l2(v[:n][mask], v_ref[mask]))
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    tol = _tol(p)
+    assert np.isfinite(y).all()
+    assert rel_l2(y, ref) <= tol, (case, rel_l2(y, ref))
+    assert row_rel_l2(y, ref) <= tol
+    # inactive rows get the base product only (the in-launch plan never splits
+    # k, so its rounding can differ from a base-only call that does: compared
+    # by value against the oracle's base rows)
+    live = oracle.live_rows(w.ids, w.active)
+    if (~live).any():
+        base_ref = oracle.base_output(dp.x_host, dp.w0_host)
+        assert row_rel_l2(y[~live], base_ref[~live]) <= tol
+    y2, v2 = _fused_in_launch(dp, seg, w)
+    assert np.array_equal(y2, y) and np.array_equal(v2[:n][mask], v[:n][mask])
+    if p.base_dtype == "fp8":
+        # W8A8: the shrink reads the unquantised x (a launch of its own first)
+        y8, _ = _fused_in_launch(dp, seg, w, flags=agm.FLAG_ACT_QUANT_E4M3)
+        ref8 = oracle.linear_w8a8(dp.x_host, dp.w0_host[0], dp.w0_host[1], *dp.oracle_args(w)[1:])
+        assert rel_l2(y8, ref8) <= TOL["bf16"] and row_rel_l2(y8, ref8) <= TOL["bf16"]
+
+
 # ---- several output slices of one x in one launch (q / k / v, gate / up) -------
 
 # merged launches on 64- and 256-row tiles with ragged slice ends, a shape
