@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--separate-build", action="store_true",
                     help="segment build and shrink as two launches also for small batches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--shrink-in-launch", action="store_true",
+                    help="headline: each one-projection fused call computes its shrink in the same launch")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -318,7 +320,8 @@ def roofline(bytes_, flops, seconds, base, mfma_dtype, kernel, traffic_key, laun
     return roof
 
 
-def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, separate_build: bool):
+def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, separate_build: bool,
+               in_launch: bool = False):
     """The whole hot path, one step per batch: device segment build -> shrink
     -> fused linear for every projection (projections of one input share a
     sliced launch).  Returns the step time from K back-to-back steps between
@@ -329,7 +332,17 @@ def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, sepa
     groups = S.groups(slices)
     S.group_workspaces(groups, flags)
     n_proj, n_groups = len(S.names), len(groups)
-    combined = not separate_build and 1 <= T <= 256 and S.n_slots <= 1024
+    # in_launch: each one-projection group's shrink runs inside its fused
+    # launch ("EpiLoRA" 3.1, the decode path); the segment build is its own launch
+    fl_one = flags | (agm.FLAG_SHRINK_IN_LAUNCH if in_launch else 0)
+    if in_launch:
+        for it in S.insts:
+            for c in it["inst"]:
+                if fl_one not in c["wsp"]:
+                    p = c["p"]
+                    c["wsp"][fl_one] = agm.fused_workspace(T, p.d_in, p.d_out, S.bt_of[p.base_dtype], fl_one,
+                                                           device="cuda:0")
+    combined = not separate_build and not in_launch and 1 <= T <= 256 and S.n_slots <= 1024
     j_first = groups[0][0]
     stream = torch.cuda.current_stream()
     gkey = (tuple(map(tuple, groups)), flags)
@@ -349,7 +362,7 @@ def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, sepa
         for gi, g in enumerate(groups):
             x = inst[g[0]]["x"]
             for j in g:
-                if combined and j == j_first:
+                if (combined and j == j_first) or (in_launch and len(g) == 1):
                     continue
                 c = inst[j]
                 if ev is not None:
@@ -361,7 +374,8 @@ def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, sepa
                 ev["fused"][gi][0].record(stream)
             if len(g) == 1:
                 c = inst[g[0]]
-                agm.fused_linear(c["base"], c["pool"], seg, x, c["v"], c["y"], flags=flags, workspace=c["wsp"][flags])
+                agm.fused_linear(c["base"], c["pool"], seg, x, c["v"], c["y"], flags=fl_one,
+                                 workspace=c["wsp"][fl_one])
             else:
                 agm.fused_linear_slices([inst[j]["base"] for j in g], [inst[j]["pool"] for j in g], seg, x,
                                         [inst[j]["v"] for j in g], [inst[j]["y"] for j in g], flags=flags,
@@ -391,7 +405,8 @@ def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, sepa
     for ev in evs:
         per["seg"] += ev["seg"][0].elapsed_time(ev["seg"][1])
         for j in range(n_proj):
-            if not (combined and j == j_first):
+            if not (combined and j == j_first) and not (in_launch and any(len(g) == 1 and g[0] == j
+                                                                          for g in groups)):
                 per["shrink"] += ev["shrink"][j][0].elapsed_time(ev["shrink"][j][1])
         for gi in range(n_groups):
             d = ev["fused"][gi][0].elapsed_time(ev["fused"][gi][1])
@@ -408,15 +423,18 @@ def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, sepa
                     "fused_f32_kernel" if base == "fp32" else DOMINANT, S.w.name + ("_w8a8" if w8a8 else ""),
                     n_groups)
     shrink_s = (per["shrink"] + (per["seg"] if combined else 0.0)) * 1e-3
-    shrink_gbs = alg["shrink_bytes"] / shrink_s / 1e9
+    # (in_launch: no shrink launch of its own; its bytes are inside the fused time)
+    shrink_gbs = alg["shrink_bytes"] / shrink_s / 1e9 if shrink_s > 0 else 0.0
     names = S.names
     return {
         "ms_per_step": ms_step,
         "value": T / (ms_step * 1e-3),
         "combined": combined,
         "groups": groups,
-        "path": ("build_shrink_dev (one launch)" if combined else "build_segments_dev -> shrink (persistent)")
-                + " -> fused_linear"
+        "path": ("build_shrink_dev (one launch)" if combined else
+                 ("build_segments_dev -> fused_linear with the shrink in the same launch" if in_launch else
+                  "build_segments_dev -> shrink (persistent)"))
+                + ("" if in_launch else " -> fused_linear")
                 + (" (one sliced launch per group: " + ", ".join("/".join(names[j] for j in g)
                                                                 for g in groups if len(g) > 1) + ")"
                    if any(len(g) > 1 for g in groups) else "")
@@ -550,7 +568,8 @@ def main():
 
     # ---- the headline workload -------------------------------------------
     S = Setup(args.config, args, flags_list=(flags,))
-    r = fused_path(S, args.steps, args.warmup, flags, not args.no_slices, args.separate_build)
+    r = fused_path(S, args.steps, args.warmup, flags, not args.no_slices, args.separate_build,
+                   in_launch=args.shrink_in_launch)
     if args.calibrate_copy_mb:
         src = torch.empty(args.calibrate_copy_mb << 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
@@ -601,6 +620,10 @@ def main():
         if name == "fp8_fused":
             per_cfg["fp8_fused_w8a8"] = _cfg_entry(fused_path(Sc, steps_c, warm_c, agm.FLAG_ACT_QUANT_E4M3, True,
                                                               args.separate_build))
+        if name in ("decode_bgmv", "fp8_fused"):
+            # the shrink inside the fused launch, against the separate launches above
+            per_cfg[name + "_shrink_in_launch"] = _cfg_entry(
+                fused_path(Sc, steps_c, warm_c, 0, not args.no_slices, args.separate_build, in_launch=True))
         if name == "decode_bgmv":
             per_cfg[name]["unfused_shrink_expand"] = unfused_adapter(
                 Sc, steps_c, warm_c, (agm.LAUNCH_PERSISTENT, agm.LAUNCH_EXACT, agm.LAUNCH_BUCKETED,
