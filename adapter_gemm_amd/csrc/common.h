@@ -126,7 +126,15 @@ struct FusedPlan {
   bool persist;        // more tiles than CUs, no split: a workgroup per CU claims tiles
   int xrow = 128;      // x bytes per row per k-step (64: bf16 256 x 256 tiles with a 4-slot ring)
   size_t ovl_bytes = 0;  // in-launch shrink: its claim / done / error counters
+  bool apipe = false;    // the adapter term as pipelined steps from packed per-tile records
+  size_t apk_bytes = 0;  // those records (every slice of the launch)
 };
+// workspace bytes of the pipelined kernel's parts of a plan, and the offset of
+// its packed adapter records within them
+size_t fused_dma_ws_bytes(const FusedPlan& pl);
+// packed adapter records of a bf16 launch of n slices over T rows, at most
+size_t fused_apk_bound(int T, int n_slices);
+size_t fused_dma_apk_offset(const FusedPlan& pl);
 
 // The shrink run inside a fused launch (LORA_FLAG_SHRINK_IN_LAUNCH): its
 // input x (the unquantised bf16 activations) and the rank-block geometry of

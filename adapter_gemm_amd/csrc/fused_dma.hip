@@ -98,7 +98,25 @@ struct DmaArgs {
   int n_prod;
   int32_t* ovc;           // {claimed, done, error}, cleared before the launch
   ShrinkArgs sh;
+  // packed adapter steps (bf16 tiles of 128+ rows): one record of apk_rec
+  // bytes per (slice, row tile), written by pack_adapter_kernel; NULL: none
+  const uint8_t* apk;
+  size_t apk_rec;
 };
+
+// Record of one (slice, row tile) in the packed adapter area:
+//   [0, 64)     int32 n: adapter steps of 64 packed ranks (0: no live row;
+//               -1: more than kApChunks chunks, the tile takes the
+//               unpacked adapter phase)
+//   [64, 320)   kApChunks x {uint32 B byte offset of the chunk's 8 ranks of
+//               channel 0 (0xffffffff: none), uint32 ranks of the chunk
+//               below the adapter's rank (1..8)}
+//   [320, ...)  BM rows x kApCap bf16: packed s_g v of the row's group at its
+//               chunks, zeros elsewhere
+constexpr int kApChunks = 32;               // packed chunks of 8 ranks per tile, at most
+constexpr int kApCap = kApChunks * 8;       // packed ranks per row
+constexpr int kApHdr = 320;
+inline size_t apk_rec_bytes(int bm) { return ((size_t)kApHdr + (size_t)bm * kApCap * 2 + 255) / 256 * 256; }
 
 constexpr int kSc1 = 16;                    // cache-policy bits of a device-coherent (sc1) buffer access
 constexpr long kOvlSpinLimit = 1L << 22;    // bound of a tile's wait for the in-launch shrink (seconds)
@@ -241,6 +259,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   __shared__ int g_row0[BM], g_row1[BM], g_rank[BM], t_rowseg[BM];
   __shared__ float g_scale[BM];
   __shared__ int s_flag, s_claim, s_sums[NW];
+  __shared__ uint32_t a_boff[kApChunks];      // packed adapter steps: B offset and rank limit per chunk
+  __shared__ int a_lim[kApChunks];
   // (decode tiles) fp32 v rows of the tile for the per-output adapter epilogue
   constexpr bool kRowEpi = BM == 64 && MODE == kBF16;
   __shared__ __attribute__((aligned(16))) float v_rows[kRowEpi ? BM * 16 : 4];
@@ -352,12 +372,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     tn = in / gm;
   }
   int n0 = tn * BN;
+  int slice_idx = 0;
   if (a.n_slices > 1) {
     // constant indices keep the slice fields in scalar registers
     SliceArgs q = a.sl[0];
 #pragma unroll
     for (int s = 1; s < kMaxSlices; ++s)
-      if (s < a.n_slices && tn >= a.sl[s].tn0) q = a.sl[s];
+      if (s < a.n_slices && tn >= a.sl[s].tn0) {
+        q = a.sl[s];
+        slice_idx = s;
+      }
     a.W = q.W;
     a.w_scale = q.w_scale;
     a.B = q.B;
@@ -387,6 +411,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   SegPtrs P;
   const bool seg_given = a.seg != nullptr;
   int s_err = 0, s_rows = 0, s_nact = 0, rowseg_ld = -1;
+  // (bf16 tiles of 128+ rows) the adapter term as extra k-steps of the main
+  // pipeline, from the packed record of this tile: the s v slab through the
+  // x slot, B slices through the W slot
+  constexpr bool kAPipe = MODE == kBF16 && BM >= 128;
+  const uint8_t* arec = nullptr;
+  int ap_n = 0;
+  uint32_t ap_boff = 0xffffffffu, ap_lim = 0;
   int perm_q[LX];
   int oseg[kRowEpi ? TM * 4 : 1];             // (decode tiles) segment of each output row of this lane
 #pragma unroll
@@ -413,6 +444,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
       for (int q = 0; q < TM * 4; ++q) asm volatile("" ::"v"(oseg[q]));
     }
+    if constexpr (kAPipe) {
+      // the packed adapter record's step count and chunk table, in the same round
+      if (a.apk != nullptr) {
+        arec = a.apk + (size_t)(slice_idx * a.tiles_m + tm) * a.apk_rec;
+        ap_n = *reinterpret_cast<const int32_t*>(arec);
+        if (tid < kApChunks) {
+          ap_boff = reinterpret_cast<const uint32_t*>(arec + 64)[2 * tid];
+          ap_lim = reinterpret_cast<const uint32_t*>(arec + 64)[2 * tid + 1];
+        }
+        asm volatile("" ::"v"(ap_boff), "v"(ap_lim));
+      }
+    }
 #pragma unroll
     for (int q = 0; q < LX; ++q) asm volatile("" ::"v"(perm_q[q]));   // keep the round together
     asm volatile("" ::"v"(rowseg_ld), "s"(s_err), "s"(s_rows), "s"(s_nact));
@@ -430,6 +473,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // the adapter phase's row -> segment ids, fetched now and used after the
   // main loop
   const bool do_lora = has_seg && a.B != nullptr && (a.lora_split ? split == a.splits : true);
+  // packed adapter steps of this tile (n_as > 0), or the unpacked phase after
+  // the main loop (old_phase)
+  int n_as = 0;
+  bool old_phase = do_lora;
+  if constexpr (kAPipe) {
+    if (do_lora && arec != nullptr) {
+      const int n = __builtin_amdgcn_readfirstlane(ap_n);
+      if (n >= 0) {
+        n_as = n;
+        old_phase = false;
+      }
+    }
+  }
   int n_active = 0, my_rowseg = -1;
   if (do_lora) {
     n_active = s_nact;
@@ -529,6 +585,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 #pragma unroll
     for (int q = 0; q < L; ++q) issue_part(kt, slot, q);
   };
+  // DMA operation q of packed adapter step p (64 packed ranks): the x slot
+  // takes the record's s v columns [64p, 64p + 64) of the tile's rows, the W
+  // slot the matching B ranks of the tile's channels (chunk table in LDS)
+  const i32x4_t aprs = rsrc(arec, kAPipe && arec ? (uint32_t)a.apk_rec : 0u);
+  const i32x4_t bprs = rsrc(a.B, kAPipe ? a.b_bytes : 0u);
+  auto issue_apart = [&](int p, int slot, int q) {
+    uint8_t* st = ring + slot * STAGE;
+    if (q < LX) {
+      const int s = (wave * LX + q) * 64 + lane;
+      const int row = s / (XROW / 16), c = swz_src<XROW>(row, s % (XROW / 16));
+      dma16(aprs, st + (wave * LX + q) * 1024, (uint32_t)(kApHdr + row * (kApCap * 2) + p * 128 + c * 16), 0u);
+    } else {
+      const int qq = q - LX;
+      const int s = (wave * LW + qq) * 64 + lane;
+      const int row = s / (WROW / 16), c = swz_src<WROW>(row, s % (WROW / 16));
+      const uint32_t bo = a_boff[p * 8 + c];
+      const int n = n0 + row;
+      const uint32_t o = (bo != 0xffffffffu && n < a.d_out) ? bo + (uint32_t)n * (uint32_t)a.r_cap * 2u : kOOB;
+      dma16(bprs, st + XS + (wave * LW + qq) * 1024, o, 0u);
+    }
+  };
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -540,8 +617,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // the MFMA blocks (kt_next < 0: none), so that a wave never stalls on a
   // burst of vector-memory issues while its matrix core could be busy
   // DMA operations per fragment block: a 2-slot ring gives the next step's
-  // loads one step to land, so they all go out in the first half of it
-  constexpr int DPB = STAGES == 2 ? 2 : 1;
+  // loads one step to land, so they all go out before its first MFMAs
+  // (measured: spreading them over the first half of the step is slower)
+  constexpr int DPB = STAGES == 2 ? L : 1;
   auto compute = [&](int slot, int kt_next, int slot_next) {
     const uint8_t* As = ring + slot * STAGE;
     const uint8_t* Ws = As + XS;
@@ -612,6 +690,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           const int row = wn * WN + j * 16 + frow;
           fb[j] = *reinterpret_cast<const bf16x8_t*>(Ws + swz<XROW>(row, kk * 4 + fk));
         }
+
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -631,17 +710,93 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   };
 
   // ---- main loop -----------------------------------------------------------
+  if constexpr (kAPipe) {
+    if (n_as > 0) {
+      // the chunk table into LDS for the adapter steps' B offsets and masks
+      if (tid < kApChunks) {
+        a_boff[tid] = ap_boff;
+        a_lim[tid] = (int)ap_lim;
+      }
+      lds_barrier();
+    }
+  }
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < nsteps) issue(kbeg + p, p);
+  // (the adapter steps continue the same slot sequence: step nsteps + p of
+  // the tile is adapter step p, and the last base steps already issue the
+  // first adapter steps' loads)
+  const int total = nsteps + n_as;
+  if constexpr (kAPipe) {
+    if (n_as > 0) {
+#pragma unroll
+      for (int p = 0; p < STAGES - 1; ++p)
+        if (p >= nsteps && p < total) {
+#pragma unroll
+          for (int q = 0; q < L; ++q) issue_apart(p - nsteps, p, q);
+        }
+    }
+  }
   for (int t = 0; t < nsteps; ++t) {
-    wait_step<L, STAGES - 2>(min(STAGES - 2, nsteps - 1 - t));
+    wait_step<L, STAGES - 2>(min(STAGES - 2, total - 1 - t));
     const bool more = t + STAGES - 1 < nsteps;
+    if constexpr (kAPipe) {
+      const int nxt = t + STAGES - 1;
+      if (nxt >= nsteps && nxt < total) {
+#pragma unroll
+        for (int q = 0; q < L; ++q) issue_apart(nxt - nsteps, nxt % STAGES, q);
+      }
+    }
     if constexpr (MODE == kBF16) {
       compute(t % STAGES, more ? kbeg + t + STAGES - 1 : -1, (t + STAGES - 1) % STAGES);
     } else {
       if (more) issue(kbeg + t + STAGES - 1, (t + STAGES - 1) % STAGES);
       compute(t % STAGES, -1, 0);
+    }
+  }
+
+  // ---- adapter steps (bf16 tiles of 128+ rows with a packed record) ---------
+  // Their own short pipeline through the same ring, after the base steps:
+  // step p multiplies the record's s v columns [64p, 64p + 64) by the matching
+  // B ranks of the tile's channels on the same accumulators.  (A separate loop
+  // keeps the base steps' code free of the rank masks.)
+  if constexpr (kAPipe) {
+    if (n_as > 0) {
+      for (int p = 0; p < n_as; ++p) {
+        const int t = nsteps + p;               // the tile's step (and slot) sequence continues
+        wait_step<L, STAGES - 2>(min(STAGES - 2, total - 1 - t));
+        if (t + STAGES - 1 < total) {
+#pragma unroll
+          for (int q = 0; q < L; ++q) issue_apart(p + STAGES - 1, (t + STAGES - 1) % STAGES, q);
+        }
+        const uint8_t* As = ring + (t % STAGES) * STAGE;
+        const uint8_t* Ws = As + XS;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8_t*>(As + swz<XROW>(wm * WM + i * 16 + frow, kk * 4 + fk));
+          // ranks of a chunk at or past its adapter's rank (pool padding)
+          // never enter the product
+          const int lim = a_lim[p * 8 + kk * 4 + fk];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            u32x4_t u = *reinterpret_cast<const u32x4_t*>(Ws + swz<XROW>(wn * WN + j * 16 + frow, kk * 4 + fk));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t keep = 2 * e >= lim ? 0u : (2 * e + 1 >= lim ? 0xffffu : 0xffffffffu);
+              u[e] &= keep;
+            }
+            fb[j] = __builtin_bit_cast(bf16x8_t, u);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
   }
 
@@ -744,7 +899,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   // k / 8 (j its rank index inside the group), else 0; packed B[n, k] is
   // B_g[n, j].  A x B^T over the packed axis is exactly the sum of the
   // groups' s_g v B_g^T, run as dense 64-wide MFMA steps.
-  if (do_lora && !row_epi) {
+  if (do_lora && !row_epi && old_phase) {
     const int pe = min(m0 + BM, n_active);
     if (m0 < pe) {
       vm_barrier<0>();                          // ring free: every wave is past its last main step
@@ -1001,6 +1156,119 @@ __global__ void zero_words_kernel(int32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// Packed adapter records for the pipelined adapter steps (workgroups of 256
+// threads, 8 rows of a row tile each; see below).  The tile's adapter groups (the segments
+// meeting its live rows) are laid end to end on one packed rank axis, each
+// padded to whole chunks of 8 ranks; a row's packed s v holds s_g v[row, j]
+// at chunk off_g + j / 8 of its own group and zeros elsewhere, so that the
+// dense product of the packed s v tile and the packed B slices over that axis
+// is exactly the sum over groups of s_g v_g B_g^T for the tile's rows.
+struct PackSlice {
+  const float* v;
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  int ld_v, r_cap, b_ch, b_n0;
+};
+struct PackArgs {
+  const int32_t* seg;
+  uint8_t* apk;
+  size_t rec;
+  int T, tiles_m;
+  PackSlice sl[kMaxSlices];
+};
+
+constexpr int kPackRows = 256 / kApChunks;   // rows of a tile per pack workgroup (one thread per chunk)
+
+// Workgroup (blockIdx.x, slice blockIdx.y) packs rows [r0, r0 + kPackRows) of
+// row tile r0 / BM: every workgroup of a tile rebuilds the tile's group table
+// (a few loads), the first one also writes the header and chunk table, and
+// each thread then writes one 16-byte chunk of one row, so that all of a
+// row's v loads and chunk stores are in flight at once.
+__global__ __launch_bounds__(256) void pack_adapter_kernel(PackArgs a, int BM) {
+  __shared__ int g_ad[kApChunks], g_rk[kApChunks], g_off[kApChunks], g_w8[kApChunks];
+  __shared__ float g_sc[kApChunks];
+  __shared__ int s_nchunks;
+  const int si = blockIdx.y, tid = threadIdx.x;
+  const int per_tile = BM / kPackRows;
+  const int tm = blockIdx.x / per_tile, r0 = (blockIdx.x - tm * per_tile) * kPackRows;
+  const PackSlice S = a.sl[si];
+  uint8_t* rec = a.apk + (size_t)(si * a.tiles_m + tm) * a.rec;
+  int32_t* hdr = reinterpret_cast<int32_t*>(rec);
+  uint32_t* tab = reinterpret_cast<uint32_t*>(rec + 64);
+  u32x4_t* vpk = reinterpret_cast<u32x4_t*>(rec + kApHdr);
+  const SegPtrs P = seg_ptrs(const_cast<int32_t*>(a.seg), a.T);
+  const bool valid = P.sum[kError] == 0 && P.sum[kRows] == a.T;
+  const int n_active = valid ? P.sum[kNActive] : 0;
+  const int m0 = tm * BM, pe = min(m0 + BM, n_active);
+  const bool lead = r0 == 0;                    // this workgroup writes the header and table
+  if (m0 >= pe) {                               // no live row in the tile
+    if (lead && tid == 0) hdr[0] = 0;
+    return;
+  }
+  const int s_first = P.pos_seg[m0], ng = P.pos_seg[pe - 1] - s_first + 1;
+  if (ng > kApChunks) {                         // more groups than chunks: the unpacked phase
+    if (lead && tid == 0) hdr[0] = -1;
+    return;
+  }
+  if (tid < ng) {
+    const int ad = P.seg_adapter[s_first + tid];
+    const int rk = S.slot_rank[ad];
+    g_ad[tid] = ad;
+    g_rk[tid] = rk;
+    g_sc[tid] = S.slot_scale[ad];
+    g_w8[tid] = (rk + 7) / 8;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int off = 0;
+    for (int g = 0; g < ng; ++g) {
+      g_off[g] = off;
+      off += g_w8[g];
+    }
+    s_nchunks = off;
+  }
+  __syncthreads();
+  const int n_chunks = s_nchunks;
+  if (n_chunks > kApChunks) {
+    if (lead && tid == 0) hdr[0] = -1;
+    return;
+  }
+  const int n_steps = (n_chunks + 7) / 8;
+  if (lead) {
+    if (tid == 0) hdr[0] = n_steps;
+    if (tid < kApChunks) {
+      uint32_t boff = 0xffffffffu, lim = 0;
+      if (tid < n_chunks) {
+        int g = 0;
+        while (g + 1 < ng && g_off[g + 1] <= tid) ++g;
+        const int j8 = tid - g_off[g];
+        boff = (uint32_t)((((size_t)g_ad[g] * S.b_ch + S.b_n0) * S.r_cap + 8 * j8) * 2);
+        lim = (uint32_t)min(8, g_rk[g] - 8 * j8);
+      }
+      tab[2 * tid] = boff;
+      tab[2 * tid + 1] = lim;
+    }
+  }
+  // chunk c of row r: the row's group's s v (fp32, scaled, rounded to bf16)
+  // at its chunks, zeros elsewhere and for rows past the live ones
+  const int r = r0 + tid / kApChunks, c = tid % kApChunks;
+  if (c >= n_steps * 8) return;
+  const int g = m0 + r < pe ? P.pos_seg[m0 + r] - s_first : -1;
+  u32x4_t o = {0, 0, 0, 0};
+  if (g >= 0 && c >= g_off[g] && c < g_off[g] + g_w8[g]) {
+    const int j8 = c - g_off[g];
+    const int lim = min(8, g_rk[g] - 8 * j8);
+    const float sc = g_sc[g];
+    const float* vr = S.v + (size_t)(m0 + r) * S.ld_v + 8 * j8;
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = e < lim ? sc * vr[e] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
+  }
+  vpk[(size_t)r * (kApCap / 8) + c] = o;
+}
+
 // CUs of the current device, 256 if the
 // query fails
 int device_cus() {
@@ -1108,6 +1376,20 @@ bool lora_fits(int bm, int bn, bool w8a16, int stages, int r_cap, int xrow = 128
 
 int fused_device_cus() { return device_cus(); }
 
+size_t fused_apk_bound(int T, int n_slices) {
+  size_t b = 0;
+  for (int bm : {128, 256}) b = std::max(b, (size_t)n_slices * ((T + bm - 1) / bm) * apk_rec_bytes(bm));
+  return b;
+}
+
+// [partials][counters][in-launch shrink counters][packed adapter records (256-byte aligned)]
+size_t fused_dma_apk_offset(const FusedPlan& pl) {
+  return (pl.part_bytes + pl.counter_bytes + pl.ovl_bytes + 255) / 256 * 256;
+}
+size_t fused_dma_ws_bytes(const FusedPlan& pl) {
+  return pl.apk_bytes ? fused_dma_apk_offset(pl) + pl.apk_bytes : pl.part_bytes + pl.counter_bytes + pl.ovl_bytes;
+}
+
 bool fused_ovl_supported(const FusedPlan& pl, int base_dtype, int flags) {
   return (flags & LORA_FLAG_SHRINK_IN_LAUNCH) && pl.dma && pl.bm <= 128 && pl.splits == 1 && pl.lora_split == 0 &&
          (base_dtype == LORA_BF16 || (base_dtype == LORA_FP8_E4M3 && !(flags & LORA_FLAG_ACT_QUANT_E4M3)));
@@ -1175,6 +1457,11 @@ FusedPlan plan_fused(int T, int d_in, int d_out, int base_dtype, int flags, int 
   pl.counter_bytes = S_total > 1 ? (size_t)pl.tiles * sizeof(int32_t)
                                  : (pl.persist ? kPersistCounters * sizeof(int32_t) : 0);
   pl.ovl_bytes = fused_ovl_supported(pl, base_dtype, flags) && r_cap > 0 ? 64 : 0;
+  // the adapter term as pipelined steps: bf16 tiles of 128+ rows, one
+  // workgroup per tile, v given on entry (not computed in the launch)
+  pl.apipe = r_cap > 0 && base_dtype == LORA_BF16 && pl.bm >= 128 && S_total == 1 &&
+             !(flags & LORA_FLAG_SHRINK_IN_LAUNCH);
+  pl.apk_bytes = pl.apipe ? (size_t)pl.tiles_m * apk_rec_bytes(pl.bm) : 0;
   return pl;
 }
 
@@ -1186,8 +1473,7 @@ size_t fused_quant_bytes(int T, int d_in, int flags, int base_dtype) {
 
 size_t fused_workspace_bytes(int T, int d_in, int d_out, int base_dtype, int flags, int r_cap) {
   const FusedPlan pl = plan_fused(T, d_in, d_out, base_dtype, flags, r_cap);
-  return fused_quant_bytes(T, d_in, flags, base_dtype) +
-         (pl.dma ? pl.part_bytes + pl.counter_bytes + pl.ovl_bytes : 0);
+  return fused_quant_bytes(T, d_in, flags, base_dtype) + (pl.dma ? fused_dma_ws_bytes(pl) : 0);
 }
 
 bool fused_dma_fits(const FusedPlan& pl, int T, int ld_x, int d_out, int ld_w, int base_dtype, int flags,
@@ -1219,6 +1505,7 @@ FusedPlan plan_fused_slices(int T, int d_in, const FusedSlice* sl, int n, int ba
     if (pl.splits > 1 || n > kMaxSlices) pl.dma = false;
     pl.persist = pl.splits == 1 && pl.lora_split == 0 && pl.bm < 256 && pl.tiles > kPersistMinTiles;
     pl.counter_bytes = pl.persist ? kPersistCounters * sizeof(int32_t) : 0;
+    pl.apk_bytes *= n;
   }
   return pl;
 }
@@ -1288,6 +1575,29 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
   a.lora_split = sl[0].pool ? pl.lora_split : 0;
   a.n_work = pl.tiles * (a.splits + a.lora_split);
   a.n_slices = n > 1 ? n : 1;
+  a.apk = nullptr;
+  a.apk_rec = 0;
+  // Packed adapter steps pay for their pack launch when tiles hold few groups:
+  // batches of at least 32 rows per usable slot on average (prefill); batches
+  // of mostly one- or two-row groups (decode, mixed layers) keep the unpacked
+  // phase, whose waves skip the fragments a group does not meet.
+  if (pl.apipe && sl[0].pool && (long)T >= 32L * std::min(T, sl[0].pool->n_slots)) {
+    PackArgs pk;
+    pk.seg = seg;
+    pk.apk = static_cast<uint8_t*>(part_ws) + fused_dma_apk_offset(pl);
+    pk.rec = apk_rec_bytes(pl.bm);
+    pk.T = T;
+    pk.tiles_m = pl.tiles_m;
+    for (int s = 0; s < n; ++s) {
+      const lora_pool_t& pool = *sl[s].pool;
+      pk.sl[s] = PackSlice{sl[s].v, pool.slot_rank, pool.slot_scale, sl[s].ld_v, pool.r_cap, pool.d_out, sl[s].col0};
+    }
+    hipLaunchKernelGGL(pack_adapter_kernel, dim3(pl.tiles_m * (pl.bm / kPackRows), n), dim3(256), 0, st, pk, pl.bm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.apk = pk.apk;
+    a.apk_rec = pk.rec;
+  }
   a.n_prod = 0;
   a.ovc = a.counters + pl.counter_bytes / sizeof(int32_t);
   if (ovl && sl[0].pool && n == 1 && fused_ovl_supported(pl, base.dtype, flags)) {

@@ -572,7 +572,12 @@ size_t fused_slices_workspace_bytes(int T, int d_in, const int32_t* d_out, const
   // a merged launch needs the W8A8 codes and, when persistent, 64 bytes of
   // claim counters after them; slices launched one by one use their own
   // plans' workspaces, one after another
-  size_t need = fused_quant_bytes(T, d_in, flags, base_dtype) + 64;
+  // (bf16 with pools: and after them, 256-byte aligned, the packed adapter
+  // records of every slice)
+  bool pools = false;
+  for (int s = 0; s < n; ++s) pools = pools || r_cap[s] > 0;
+  const size_t apk = pools && base_dtype == LORA_BF16 ? 256 + fused_apk_bound(T, n) : 0;
+  size_t need = fused_quant_bytes(T, d_in, flags, base_dtype) + 64 + apk;
   for (int s = 0; s < n; ++s)
     need = std::max(need, fused_workspace_bytes(T, d_in, d_out[s], base_dtype, flags, r_cap[s]));
   return need;

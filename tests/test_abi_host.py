@@ -224,13 +224,22 @@ def test_quant_and_dev_builder_validation():
     assert lib.lora_build_segments_dev(None, None, 8, 4, 0, FAKE, None) == agm.LORA_E_ARG
     # bf16 filling the GPU exactly once (256 tiles of 64 x 64): no workspace;
     # more 128-row tiles than CUs (3 x 96 of 128 x 128): 64 bytes of claim
-    # counters; 256-row tiles (16 x 128 of 256 x 256) stay one-shot for small
-    # rank capacities, but pools of capacity >= 96 leave no LDS for them and
-    # take persistent 128 x 128 tiles: the query covers every capacity;
-    # fp8 W8A8: codes + scales
+    # counters, and with a pool the packed adapter records of the 3 row tiles
+    # after them (256-byte aligned); 256-row tiles (16 x 128 of 256 x 256)
+    # stay one-shot (records only) for small rank capacities, but pools of
+    # capacity >= 96 leave no LDS for them and take persistent 128 x 128
+    # tiles: the query covers every capacity; fp8 W8A8: codes + scales
+    rcap = lib.lora_fused_workspace_bytes_rcap
+
+    def rec(bm):                     # one packed adapter record: 320-byte header + bm rows of 256 bf16
+        return -(-(320 + bm * 512) // 256) * 256
     assert lib.lora_fused_workspace_bytes(256, 64, 4096, agm.BF16, 0) == 0
-    assert lib.lora_fused_workspace_bytes(384, 64, 12288, agm.BF16, 0) == 64
-    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 64
+    assert rcap(384, 64, 12288, agm.BF16, 0, 0) == 64
+    assert rcap(384, 64, 12288, agm.BF16, 0, 8) == 256 + 3 * rec(128)
+    assert rcap(4096, 64, 32768, agm.BF16, 0, 0) == 0
+    assert rcap(4096, 64, 32768, agm.BF16, 0, 8) == 16 * rec(256)
+    assert rcap(4096, 64, 32768, agm.BF16, 0, 128) == 256 + 32 * rec(128)
+    assert lib.lora_fused_workspace_bytes(4096, 64, 32768, agm.BF16, 0) == 256 + 32 * rec(128)
     assert lib.lora_fused_workspace_bytes(4, 64, 64, agm.FP8_E4M3, agm.FLAG_ACT_QUANT_E4M3) >= 4 * 64 + 16
     # a small output (10 tiles of 64 x 64): 2 k splits + 1 adapter split per tile
     assert lib.lora_fused_workspace_bytes(100, 1024, 264, agm.BF16, 0) == 10 * 3 * 64 * 64 * 4 + 10 * 4
@@ -248,9 +257,11 @@ def test_fused_slices_host_checks():
                lib.lora_fused_workspace_bytes(100, 1024, 136, agm.BF16, 0))
     assert lib.lora_fused_slices_workspace_bytes(2, 100, 1024, d, agm.BF16, 0) == lone > 0
     # a merged launch needs no partial tiles, only the claim counters of a
-    # persistent launch (64 bytes)
+    # persistent launch (64 bytes) and, 256-byte aligned, the packed adapter
+    # records of every slice (at most 3 slices x 16 row tiles of 128 rows)
     big = (ctypes.c_int32 * 3)(4096, 1024, 1024)
-    assert lib.lora_fused_slices_workspace_bytes(3, 2048, 4096, big, agm.BF16, 0) == 64
+    rec128 = -(-(320 + 128 * 512) // 256) * 256
+    assert lib.lora_fused_slices_workspace_bytes(3, 2048, 4096, big, agm.BF16, 0) == 64 + 256 + 3 * 16 * rec128
     # errors: no slices; base dtypes that differ
     E_ARG, E_DTYPE = 1, 4
     assert lib.lora_fused_linear_slices(0, None, None, None, 0, None, 0, 0, None, None, None, None, None, 0,
@@ -377,7 +388,9 @@ def test_fused_workspace_query_covers_every_rank_capacity(r_cap):
         assert call(fake + 16, need) == agm.LORA_E_ALIGN
         assert call(fake + 16, any_cap) == agm.LORA_E_ALIGN
     # the 2048-row 4096 -> 4096 shape at capacity 128 runs persistent 128 x 128
-    # tiles with 64 bytes of claim counters, which capacity 8 does not need
-    assert lib.lora_fused_workspace_bytes_rcap(2048, 4096, 4096, agm.BF16, 0, 128) == 64
-    assert lib.lora_fused_workspace_bytes_rcap(2048, 4096, 4096, agm.BF16, 0, 8) == 0
-    assert lib.lora_fused_workspace_bytes(2048, 4096, 4096, agm.BF16, 0) == 64
+    # tiles with 64 bytes of claim counters (and 16 packed records), which
+    # capacity 8 (one-shot 256 x 128 tiles, 8 records) does not need
+    rec = lambda bm: -(-(320 + bm * 512) // 256) * 256
+    assert lib.lora_fused_workspace_bytes_rcap(2048, 4096, 4096, agm.BF16, 0, 128) == 256 + 16 * rec(128)
+    assert lib.lora_fused_workspace_bytes_rcap(2048, 4096, 4096, agm.BF16, 0, 8) == 8 * rec(256)
+    assert lib.lora_fused_workspace_bytes(2048, 4096, 4096, agm.BF16, 0) == 256 + 16 * rec(128)

@@ -764,6 +764,33 @@ def test_rank_edge_cases(ranks, r_cap):
     assert rel_l2(to_f64(yz), d_ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,d_out,ranks,r_cap", [(1500, 2056, [5, 17, 33, 64], 64),      # 256 x 128 tiles
+                                                  (4100, 8200, [1, 64, 9, 40], 64),       # 256 x 256 tiles
+                                                  (1100, 4104, [128, 3, 72, 100], 128)])  # persistent 128 x 128
+def test_packed_adapter_steps_ranks(T, d_out, ranks, r_cap):
+    """Prefill-shaped batches (long groups over few slots) run the adapter
+    term as pipelined steps from packed per-tile records: ranks that are not
+    multiples of 8 leave part-filled chunks whose pool padding (NaN here) must
+    never enter the product; requests of random lengths put 1 to 3 groups in
+    a tile, and some rows carry no adapter."""
+    g = np.random.default_rng(T + r_cap)
+    lens = g.integers(40, 400, 64)
+    ids = np.repeat(g.integers(-1, 4, 64), lens)[:T]
+    ids = np.concatenate([ids, np.full(T - len(ids), 2)]).astype(np.int32)
+    w = _custom(T, 512, d_out, 4, r_cap, ranks, ids)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    seg, s = segments(w, 4)
+    y = _fused(dp, seg, s, w)
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    assert np.isfinite(y).all()
+    assert rel_l2(y, ref) <= TOL["bf16"] and row_rel_l2(y, ref) <= TOL["bf16"]
+    d = _fused(dp, seg, s, w, zero_base=True)
+    d_ref = oracle.lora_delta(*dp.oracle_args(w))
+    live = oracle.live_rows(w.ids, w.active)
+    assert rel_l2(d, d_ref) <= TOL["bf16"] and row_rel_l2(d[live], d_ref[live]) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("r_cap,ranks", [(16, [16, 9, 8, 1, 5, 12]), (8, [8, 1, 3, 7, 2, 5])])
 def test_decode_tile_epilogue_ranks(r_cap, ranks):
     """64 x 64 bf16 tiles with rank capacity <= 16 take the per-output adapter
