@@ -257,6 +257,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
   __shared__ int g_row0[BM], g_row1[BM], g_rank[BM], t_rowseg[BM];
+  __shared__ int t_perm[BM == 64 ? 1 : BM];   // token row of each tile row (-1 past T)
   __shared__ float g_scale[BM];
   __shared__ int s_flag, s_claim, s_sums[NW];
   __shared__ uint32_t a_boff[kApChunks];      // packed adapter steps: B offset and rank limit per chunk
@@ -571,6 +572,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     c = swz_src<WROW>(row, s % (WROW / 16));
     const int n = n0 + row;
     woff[q] = n < a.d_out ? (uint32_t)(n * a.ld_w * WE + c * 16) : kOOB;
+  }
+  // the tile's token rows for the output stage, one lane per row
+  if constexpr (BM != 64) {
+#pragma unroll
+    for (int q = 0; q < LX; ++q) {
+      const int s = (wave * LX + q) * 64 + lane;
+      if (s % (XROW / 16) == 0) {
+        const int row = s / (XROW / 16), pos = m0 + row;
+        t_perm[row] = pos < a.T ? (has_seg ? perm_q[q] : pos) : -1;
+      }
+    }
   }
   const i32x4_t xrs = rsrc(a.x, a.x_bytes);
   const i32x4_t wrs = rsrc(a.W, a.w_bytes);
@@ -1134,20 +1146,60 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     }
     if (tid == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // 128- and 256-row tiles go through LDS: each wave writes its bf16 outputs
+  // into a private region of the ring (free now), then stores whole 16-byte
+  // row chunks, 16 lanes per row of the wave's columns, instead of 2 bytes
+  // per lane and instruction.  Chunk c of row r sits at c ^ (2 ((r >> 2) mod
+  // 4)) (within the row), so that the 4 rows of one fragment write land on
+  // distinct LDS banks.  (64-row decode tiles store directly: a handful of
+  // stores per lane, and no barrier behind the slowest wave's epilogue.)
+  if constexpr (BM == 64) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = row_base + i * 16 + orow + e;
-      if (pos >= a.T) continue;
-      const int row = has_seg ? P.perm[pos] : pos;
-      uint16_t* yr = Y + (size_t)row * a.ld_y;
+      for (int e = 0; e < 4; ++e) {
+        const int pos = row_base + i * 16 + orow + e;
+        if (pos >= a.T) continue;
+        const int row = has_seg ? P.perm[pos] : pos;
+        uint16_t* yr = Y + (size_t)row * a.ld_y;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = col_base + j * 16 + ocol;
-        if (n < a.d_out) yr[n] = f32_to_bf16(acc[i][j][e]);
+        for (int j = 0; j < TN; ++j) {
+          const int n = col_base + j * 16 + ocol;
+          if (n < a.d_out) yr[n] = f32_to_bf16(acc[i][j][e]);
+        }
       }
     }
+  } else {
+  static_assert(BM * BN * 2 <= RING, "the bf16 output tile fits the ring");
+  lds_barrier();                                // every wave is past its last ring read
+  {
+    constexpr int RB = WN * 2, NCH = WN / 8;    // bytes and 16-byte chunks per row of the wave
+    static_assert((WM * NCH) % 64 == 0, "whole store rounds per wave");
+    uint8_t* ob = ring + wave * (WM * RB);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + orow + e;
+        const int key = (2 * ((r >> 2) & 3)) & (NCH - 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = j * 16 + ocol;
+          *reinterpret_cast<uint16_t*>(ob + r * RB + (((c >> 3) ^ key) << 4) + (c & 7) * 2) =
+              f32_to_bf16(acc[i][j][e]);
+        }
+      }
+#pragma unroll
+    for (int t = 0; t < WM * NCH / 64; ++t) {
+      const int ch = t * 64 + lane;
+      const int r = ch / NCH, c = ch % NCH;
+      const int key = (2 * ((r >> 2) & 3)) & (NCH - 1);
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ob + r * RB + ((c ^ key) << 4));
+      const int trow = t_perm[wm * WM + r];
+      const int n = col_base + c * 8;
+      if (trow >= 0 && n < a.d_out) st128(Y + (size_t)trow * a.ld_y + n, val);
+    }
+  }
   }
   }  // work items
 }
