@@ -153,6 +153,39 @@ def test_device_segments_small_batch_kernel(order):
         _check_layout(ids, np.ones(T, np.uint8), N, order)     # flags given, all set
 
 
+@pytest.mark.parametrize("order", [0, 1])
+def test_device_segments_wave_range_builder(order):
+    """Batches of 2049 .. 16384 rows over at most 1024 adapters take the
+    builder whose 16 waves each own one contiguous row range: its edges (and
+    just past them, the chunked builder), segments that cross wave ranges,
+    ragged T, inactive rows, Zipf-skewed ids and every field of the layout
+    against the oracle's grouping, in both segment orders."""
+    g = np.random.default_rng(31 + order)
+    cases = [
+        (2049, 128, g.integers(-1, 128, 2049), None),                              # first size it takes
+        (16384, 1024, g.integers(-1, 1024, 16384), g.uniform(size=16384) > 0.3),  # largest batch and pool
+        (16385, 64, g.integers(-1, 64, 16385), None),                             # one past: chunked builder
+        (5000, 1025, g.integers(-1, 1025, 5000), None),                           # pool one past: chunked
+        (8192, 128, np.repeat(g.integers(-1, 128, 32), 256), None),               # request runs over waves
+        (3001, 40, np.minimum(g.zipf(1.2, 3001) - 1, 39), g.uniform(size=3001) > 0.1),
+        (4097, 7, np.full(4097, 6), None),                                        # one adapter everywhere
+        (2500, 16, g.integers(0, 16, 2500), np.zeros(2500, bool)),                # every row inactive
+        (6000, 300, np.full(6000, -1), None),                                     # no adapter anywhere
+    ]
+    for T, N, ids, act in cases:
+        ids = np.asarray(ids, np.int32)
+        if act is not None:
+            act = np.asarray(act, np.uint8)
+        _check_layout(ids, act, N, order)
+    # an out-of-range id in this builder's range is reported, as elsewhere
+    ids = g.integers(0, 50, 3000).astype(np.int32)
+    ids[2999] = 50
+    w = type("W", (), {})()
+    w.ids, w.active, w.T = ids, np.ones(3000, np.uint8), 3000
+    seg, s = segments(w, 50, order, True)
+    assert s.error == agm.LORA_E_ID
+
+
 def test_device_segments_large_and_bad_ids():
     g = np.random.default_rng(5)
     for T, N in [(1, 1), (1023, 7), (1025, 8192), (5000, 300), (20000, 1024)]:
