@@ -158,14 +158,16 @@ __device__ __forceinline__ void vm_barrier() {
 
 // Wait for the ring slot of the current step: `ahead` (0 .. MAXA) later
 // steps of L operations each may stay in flight.
-template <int L, int MAXA>
+// EXTRA: later operations of another kind (issued after this step's slab)
+// that may stay in flight as well.
+template <int L, int MAXA, int EXTRA = 0>
 __device__ __forceinline__ void wait_step(int ahead) {
-  static_assert(MAXA * L <= 63, "vmcnt counts at most 63 operations");
+  static_assert(MAXA * L + EXTRA <= 63, "vmcnt counts at most 63 operations");
   if constexpr (MAXA >= 1) {
-    if (ahead >= MAXA) { vm_barrier<MAXA * L>(); return; }
-    wait_step<L, MAXA - 1>(ahead);
+    if (ahead >= MAXA) { vm_barrier<MAXA * L + EXTRA>(); return; }
+    wait_step<L, MAXA - 1, EXTRA>(ahead);
   } else {
-    vm_barrier<0>();
+    vm_barrier<EXTRA>();
   }
 }
 
@@ -493,30 +495,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
     if (tid < BM && m0 + tid < n_active) my_rowseg = rowseg_ld;
   }
 
-  // (decode tiles, ranks <= 16) the per-output adapter epilogue's operands go
-  // out now and land while the main loop runs: one more dependent round here
-  // (each output row's adapter), then its rank, scale and the B rank rows of
-  // this lane's outputs, and the tile's fp32 v rows into LDS.  The main
-  // loop's waits count these as older operations, which complete first.
+  // (decode tiles, ranks <= 16) the per-output adapter epilogue's operands:
+  // the tile's fp32 v rows go into LDS now; each output row's adapter, then
+  // its rank, scale and the B rank rows of this lane's outputs are loaded
+  // right after the first slabs' DMA (load_row_epi below), so that their
+  // dependent round trips run beside the slabs' and land while the main loop
+  // runs.  The waits of the first STAGES - 1 steps allow for them.
   bool row_epi = false;
   int ad_o[kRowEpi ? TM * 4 : 1], rk_o[kRowEpi ? TM * 4 : 1];
   float sc_o[kRowEpi ? TM * 4 : 1];
   u32x4_t bq[kRowEpi ? TM * 4 : 1][kRowEpi ? TN : 1][2];
+  // vector loads load_row_epi issues (every one unconditional)
+  constexpr int kEpiLoads = kRowEpi ? TM * 4 * (3 + 2 * TN) : 0;
   if constexpr (kRowEpi) {
     row_epi = do_lora && a.r_cap <= 16;
-    // every load below is unconditional, from an address clamped into the
-    // pool (adapter 0, channel 0 where there is nothing to read), and what
-    // it returns is masked only where it is used: a load under a branch
-    // would make the compiler wait for it before the branches join
+    if (row_epi && m0 < min(m0 + BM, n_active) && !OVL) {
+      // raw fp32 v rows [m0, min(m0 + BM, n_active)) x r_cap (rows past it: zeros)
+      const int pe = min(m0 + BM, n_active);
+      const int rq = a.r_cap / 4;
+      const i32x4_t vrs = rsrc(a.v, a.v_bytes);
+      for (int c0 = wave * 64; c0 < BM * rq; c0 += NT) {
+        const int c = c0 + lane;
+        const int row = c / rq, c4 = c - row * rq;
+        const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
+        dma16(vrs, reinterpret_cast<uint8_t*>(v_rows) + c0 * 16, o, 0u);
+      }
+    }
+  }
+  auto load_row_epi = [&]() {
+    // every load below is unconditional (kEpiLoads of them), from an address
+    // clamped into its buffer (adapter 0, channel 0 where there is nothing
+    // to read) or from an empty range, which returns zeros without touching
+    // memory; what it returns is masked only where it is used
+    const __amdgpu_buffer_rsrc_t adr = __builtin_amdgcn_make_buffer_rsrc(
+        has_seg ? static_cast<void*>(P.seg_adapter) : nullptr, 0, has_seg ? a.T * 4 : 0, kBufferWord3);
 #pragma unroll
     for (int q = 0; q < TM * 4; ++q) {
       const int r = wm * WM + (q >> 2) * 16 + (lane >> 4) * 4 + (q & 3);
       const bool live = row_epi && m0 + r < n_active && oseg[q] >= 0;
-      const int ad = has_seg ? P.seg_adapter[max(oseg[q], 0)] : 0;
+      const int ad = (int)__builtin_amdgcn_raw_buffer_load_b32(adr, max(oseg[q], 0) * 4, 0, 0);
       ad_o[q] = live ? ad : -1;
     }
-    // buffer loads: without a pool (row_epi false) the ranges are empty and
-    // every load returns zeros without touching memory
+    // without a pool (row_epi false) the ranges are empty
     const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t*>(a.slot_rank), 0, row_epi ? 0x7fffffff : 0, kBufferWord3);
     const __amdgpu_buffer_rsrc_t scr = __builtin_amdgcn_make_buffer_rsrc(
@@ -539,19 +559,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
           bq[q][j][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bqr, (int)o, h * 16, 0));
       }
     }
-    if (row_epi && m0 < min(m0 + BM, n_active) && !OVL) {
-      // raw fp32 v rows [m0, min(m0 + BM, n_active)) x r_cap (rows past it: zeros)
-      const int pe = min(m0 + BM, n_active);
-      const int rq = a.r_cap / 4;
-      const i32x4_t vrs = rsrc(a.v, a.v_bytes);
-      for (int c0 = wave * 64; c0 < BM * rq; c0 += NT) {
-        const int c = c0 + lane;
-        const int row = c / rq, c4 = c - row * rq;
-        const uint32_t o = (m0 + row < pe) ? (uint32_t)(((m0 + row) * a.ld_v + c4 * 4) * 4) : kOOB;
-        dma16(vrs, reinterpret_cast<uint8_t*>(v_rows) + c0 * 16, o, 0u);
-      }
-    }
-  }
+  };
 
   // per-lane DMA source offsets (k-step offsets go into soffset)
   uint32_t xoff[LX], woff[LW];
@@ -749,8 +757,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
         }
     }
   }
+  if constexpr (kRowEpi) load_row_epi();
   for (int t = 0; t < nsteps; ++t) {
-    wait_step<L, STAGES - 2>(min(STAGES - 2, total - 1 - t));
+    // (the first STAGES - 1 slabs are older than the epilogue's loads)
+    if (kEpiLoads > 0 && t < STAGES - 1) wait_step<L, STAGES - 2, kEpiLoads>(min(STAGES - 2, total - 1 - t));
+    else wait_step<L, STAGES - 2>(min(STAGES - 2, total - 1 - t));
     const bool more = t + STAGES - 1 < nsteps;
     if constexpr (kAPipe) {
       const int nxt = t + STAGES - 1;
