@@ -89,6 +89,7 @@ struct DmaArgs {
   int r_cap, ld_v, ld_y, ld_x, ld_w, T, d_in, d_out;
   int b_ch, b_n0;         // B pool channels per slot, and the first channel of these outputs
   int tiles_m, tiles_n, group_m, nk, splits, lora_split;
+  int lpt_cols;           // (persistent) columns per XCD of the row-tile-weight claim order, else 0
   int n_work;             // work items: tiles x (splits + lora_split)
   int n_slices;           // > 1: the per-slice fields above come from sl[]
   SliceArgs sl[kMaxSlices];
@@ -262,6 +263,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   __shared__ int t_perm[BM == 64 ? 1 : BM];   // token row of each tile row (-1 past T)
   __shared__ float g_scale[BM];
   __shared__ int s_flag, s_claim, s_sums[NW];
+  __shared__ int s_order[8];                  // row tiles, most adapter groups first
+  __shared__ int s_lpt;                       // the weights differ: claim in that order
   __shared__ uint32_t a_boff[kApChunks];      // packed adapter steps: B offset and rank limit per chunk
   __shared__ int a_lim[kApChunks];
   // (decode tiles) fp32 v rows of the tile for the per-output adapter epilogue
@@ -346,6 +349,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
 
   const int S_total = a.splits + a.lora_split;
   const int full = (a.n_work / 8) * 8, per_xcd = full / 8, xcd = blockIdx.x & 7;
+  // (more tiles than CUs, at most 8 row tiles, each XCD's items whole
+  // columns) every XCD takes the row tiles with the most adapter groups
+  // first (persistent claims, or the one-shot grid's dispatch order): a
+  // tile's adapter phase grows with its groups, and a heavy tile taken last
+  // is the launch's tail.  The weight of a row tile is the number of segments
+  // meeting its live rows (0 without a valid segment buffer); ties keep the
+  // row order, so every workgroup computes the same permutation.  Equal
+  // weights keep the column-major order below (consecutive items share W0
+  // columns).
+  {
+    if (a.lpt_cols > 0 && tid < 64) {
+      int wgt = -1;
+      if (tid < a.tiles_m) {
+        wgt = 0;
+        if (a.seg != nullptr && a.B != nullptr) {
+          const SegPtrs SP = seg_ptrs(const_cast<int32_t*>(a.seg), a.T);
+          const int na = SP.sum[kError] == 0 && SP.sum[kRows] == a.T ? SP.sum[kNActive] : 0;
+          const int first = tid * BM, last = min(first + BM, na) - 1;
+          if (first <= last) wgt = SP.pos_seg[last] - SP.pos_seg[first] + 1;
+        }
+      }
+      int rank = 0, differ = 0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int wr = __shfl(wgt, r, 64);
+        if (r < a.tiles_m && tid < a.tiles_m && (wr > wgt || (wr == wgt && r < tid))) ++rank;
+        if (r < a.tiles_m && wr != __shfl(wgt, 0, 64)) differ = 1;
+      }
+      if (tid < a.tiles_m) s_order[rank] = tid;
+      if (tid == 0) s_lpt = differ;
+    }
+    if (a.lpt_cols > 0) lds_barrier();        // the order is every wave's before any maps an item
+  }
   // (persistent) a workgroup claims its next item only once it is free:
   // claiming earlier would hold an item while the adapter phase, whose
   // length varies from tile to tile, still runs
@@ -366,7 +402,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fused_dma_kernel(DmaArgs a) {
   }
   const int tile = pid / S_total, split = pid - tile * S_total;
   int tm, tn;
-  {
+  if (a.lpt_cols > 0 && pid < full && s_lpt) {
+    // XCD x's items are columns [x C, x C + C) of every row tile (C =
+    // lpt_cols), the same set as below, claimed row tile by row tile
+    const int x = pid / per_xcd, k = pid - x * per_xcd;
+    tm = s_order[k / a.lpt_cols];
+    tn = x * a.lpt_cols + k % a.lpt_cols;
+  } else {
     const int per_group = a.group_m * a.tiles_n;
     const int g = tile / per_group, first_m = g * a.group_m;
     const int gm = min(a.tiles_m - first_m, a.group_m);
@@ -1637,6 +1679,13 @@ hipError_t launch_fused_dma_slices(const FusedPlan& pl, const FusedSlice* sl, in
   a.splits = pl.splits;
   a.lora_split = sl[0].pool ? pl.lora_split : 0;
   a.n_work = pl.tiles * (a.splits + a.lora_split);
+  // heaviest row tiles first (launches of more tiles than CUs whose XCD
+  // ranges are whole columns of one row-tile group: at most 8 row tiles,
+  // per-XCD item count a multiple of them)
+  a.lpt_cols = 0;
+  if (a.splits + a.lora_split == 1 && a.n_work > fused_device_cus() && pl.tiles_m <= 8 && a.n_work % 8 == 0 &&
+      (a.n_work / 8) % pl.tiles_m == 0)
+    a.lpt_cols = a.n_work / 8 / pl.tiles_m;
   a.n_slices = n > 1 ? n : 1;
   a.apk = nullptr;
   a.apk_rec = 0;

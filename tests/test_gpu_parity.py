@@ -55,6 +55,9 @@ PIPE = {
     "decode_persistent": ("decode_bgmv", dict(T=600, d_in=1024, d_out=3000, n_slots=40)),       # 64x64, 470 tiles
     "prefill_persistent128": ("prefill_sgmv", dict(T=1100, d_in=512, d_out=4104, n_slots=24, n_req=5)),  # 128x128, 297
     "fp8_persistent": ("fp8_fused", dict(T=520, d_in=512, d_out=4112, n_slots=32, r=64)),        # 64x64 W8A16, 585
+    # persistent launches whose XCD ranges are whole columns: heaviest row tiles claimed first
+    "fp8_row_order": ("fp8_fused", dict(T=512, d_in=512, d_out=9216, n_slots=200, r=64)),        # 128x128 W8A16, 288
+    "prefill_row_order": ("prefill_sgmv", dict(T=1024, d_in=512, d_out=5120, n_slots=64, n_req=40)),  # 128x128, 320
     # W8A8 on 256 x 128 tiles (its largest), W8A16 on persistent 128 x 128 tiles
     "fp8_wide": ("fp8_fused", dict(T=600, d_in=256, d_out=16376, n_slots=32, r=64)),
     "llama_kv": ("llama_layer", dict(n_slots=96, n_req=3, prefill_len=40, n_decode=70,
