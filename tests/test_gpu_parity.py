@@ -925,3 +925,59 @@ def test_zero_B_gives_base_exactly():
     y = _fused(dp, seg, s, w)
     yb = _fused(dp, seg, s, w, with_pool=False)
     assert np.array_equal(y, yb)
+
+
+@pytest.mark.parametrize("case", ["pool_over_2GiB", "over_65535_slots"])
+def test_large_pools_take_the_general_kernel(case):
+    """Pools the pipelined kernel cannot address (B over 2 GiB for its 32-bit
+    buffer offsets; more than 65535 slots for the 16-bit slot field of its
+    chunk records) go to the general kernel; rows whose adapter sits past
+    those limits must still get the oracle's result.  Only the touched slots
+    hold values (the rest stay zero); the oracle sees those slots alone."""
+    if case == "pool_over_2GiB":
+        kw = dict(T=96, d_in=256, d_out=4096, n_slots=2100, r=128)      # B: 2.2 GB
+        far = [2099, 2050, 1200]
+    else:
+        kw = dict(T=64, d_in=128, d_out=264, n_slots=70000, r=8)
+        far = [69999, 65536, 40000]
+    w = make_workload("decode_bgmv", **kw)
+    p = w.projections[0]
+    ids = w.ids.copy()
+    live_rows = np.flatnonzero(ids >= 0)
+    for k, a in enumerate(far):                  # a few live rows on far slots
+        ids[live_rows[3 * k:3 * k + 3]] = a
+    w.ids = ids
+    touched = w.touched_slots()
+    assert max(touched) == far[0]
+    A = torch.zeros((p.n_slots, p.r_cap, p.d_in), dtype=torch.bfloat16, device=DEV)
+    B = torch.zeros((p.n_slots, p.d_out, p.r_cap), dtype=torch.bfloat16, device=DEV)
+    A_c = np.zeros((len(touched), p.r_cap, p.d_in), np.uint16)
+    B_c = np.zeros((len(touched), p.d_out, p.r_cap), np.uint16)
+    for k, a in enumerate(touched):
+        A_c[k], B_c[k] = p.slot(a)
+        A[a] = bf16_dev(A_c[k])
+        B[a] = bf16_dev(B_c[k])
+    if case == "pool_over_2GiB":
+        assert B.numel() * 2 > 0x7FFFFFFF
+    rank = torch.from_numpy(p.slot_rank.astype(np.int32)).to(DEV)
+    scale = torch.from_numpy(p.slot_scale.astype(np.float32)).to(DEV)
+    pool = agm.pool_desc(A, B, rank, scale)
+    w0 = p.w0()
+    base = agm.base_desc(bf16_dev(w0), None)
+    xh = w.x(p)
+    x = bf16_dev(xh)
+    seg, s = segments(w, p.n_slots)
+    v = torch.zeros(w.T, p.r_cap, device=DEV)
+    agm.shrink(pool, seg, w.T, s, x, v)
+    y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(torch.bfloat16)
+    ws = agm.fused_workspace(w.T, p.d_in, p.d_out, agm.BF16, 0, device=DEV)
+    agm.fused_linear(base, pool, seg, x, v, y, workspace=ws)
+    torch.cuda.synchronize()
+    remap = {a: k for k, a in enumerate(touched)}
+    ids_c = np.array([remap.get(int(a), -1) if a >= 0 else -1 for a in ids], np.int32)
+    ref = oracle.linear(xh, w0, ids_c, w.active, A_c, B_c, p.slot_rank[touched], p.slot_scale[touched])
+    got = to_f64(y)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) <= TOL["bf16"] and row_rel_l2(got, ref) <= TOL["bf16"], case
+    far_rows = np.isin(ids, far)
+    assert row_rel_l2(got[far_rows], ref[far_rows]) <= TOL["bf16"], case
