@@ -73,6 +73,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two fp8 e4m3 codes (bytes 0-1 of w, or 2-3 with HI) -> two bf16, exact: an
+// e4m3 value has at most 4 significant bits and an exponent well inside
+// bf16's range.  One v_cvt_scalef32_pk_bf16_fp8 with a unit scale (gfx950).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Workgroup barrier for data exchanged through LDS: waits for this wave's
 // LDS operations only, so global stores still in flight (which no thread of
 // the workgroup reads back) do not hold the barrier as __syncthreads() does.

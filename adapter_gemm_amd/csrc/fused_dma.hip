@@ -224,15 +224,8 @@ __device__ __forceinline__ int swz_src(int row, int cl) {
 
 // 8 e4m3 codes -> 8 bf16, exact (e4m3 values have 4 significant bits)
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint2 c) {
-  u32x4_t o;
-  const uint32_t w[2] = {c.x, c.y};
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false);
-    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);
-    o[2 * q] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
-    o[2 * q + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
-  }
+  const u32x4_t o = {e4m3x2_to_bf16x2<false>(c.x), e4m3x2_to_bf16x2<true>(c.x), e4m3x2_to_bf16x2<false>(c.y),
+                     e4m3x2_to_bf16x2<true>(c.y)};
   return __builtin_bit_cast(bf16x8_t, o);
 }
 

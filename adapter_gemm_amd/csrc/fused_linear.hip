@@ -69,16 +69,10 @@ __device__ __forceinline__ void tile_of(int pid, int nblk, int tiles_m, int tile
 
 // fp8 e4m3 x16 (one 16-byte chunk) -> bf16 x16 (two 16-byte chunks), exact.
 __device__ __forceinline__ void e4m3x16_to_bf16(const u32x4_t& c, u32x4_t& lo, u32x4_t& hi) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], false);
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], true);
-    // e4m3 values carry 4 significant bits: the upper half of the fp32 is exact
-    const uint32_t w0 = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
-    const uint32_t w1 = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
-    if (q < 2) { lo[2 * q] = w0; lo[2 * q + 1] = w1; }
-    else       { hi[2 * (q - 2)] = w0; hi[2 * (q - 2) + 1] = w1; }
-  }
+  lo = u32x4_t{e4m3x2_to_bf16x2<false>(c[0]), e4m3x2_to_bf16x2<true>(c[0]), e4m3x2_to_bf16x2<false>(c[1]),
+               e4m3x2_to_bf16x2<true>(c[1])};
+  hi = u32x4_t{e4m3x2_to_bf16x2<false>(c[2]), e4m3x2_to_bf16x2<true>(c[2]), e4m3x2_to_bf16x2<false>(c[3]),
+               e4m3x2_to_bf16x2<true>(c[3])};
 }
 
 template <int BM, int BN, int MODE>
