@@ -927,6 +927,33 @@ def test_zero_B_gives_base_exactly():
     assert np.array_equal(y, yb)
 
 
+@pytest.mark.parametrize("T,d_out", [(512, 9216),    # persistent 128 x 128 W8A16 tiles
+                                     (256, 264),     # 64 x 64 W8A16 tiles
+                                     (528, 1000)])   # d_in % 64 != 0: the general kernel
+def test_every_e4m3_code_widens_exactly(T, d_out):
+    """Widened fp8 (W8A16) with x the identity (T = d_in): y[i, n] is the
+    decoded code W0[n, i] times its channel scale, a power of two, so every
+    finite e4m3 code (all 254, subnormals and signed zeros included) must come
+    out as its exact value in bf16."""
+    d_in = T
+    n = np.arange(d_out)[:, None]
+    k = np.arange(d_in)[None, :]
+    codes = ((n * 37 + k) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00                     # the two NaN codes
+    assert len(np.unique(codes[:, :256])) == 254
+    scale = np.ldexp(1.0, (np.arange(d_out) % 5) - 2).astype(np.float32)
+    expect = (oracle.decode_e4m3(codes) * scale.astype(np.float64)[:, None]).T   # [d_in = T, d_out]
+    W = torch.from_numpy(codes).to(DEV)
+    ws = torch.from_numpy(scale).to(DEV)
+    x = torch.eye(T, dtype=torch.bfloat16, device=DEV)
+    y = torch.full((T, d_out), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wsp = agm.fused_workspace(T, d_in, d_out, agm.FP8_E4M3, 0, device=DEV)
+    agm.fused_linear(agm.base_desc(W, ws), None, None, x, None, y, workspace=wsp)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, expect)
+
+
 @pytest.mark.parametrize("case", ["pool_over_2GiB", "over_65535_slots"])
 def test_large_pools_take_the_general_kernel(case):
     """Pools the pipelined kernel cannot address (B over 2 GiB for its 32-bit
