@@ -565,6 +565,72 @@ def _slice_setup(case):
     return w, [DevProjection(w, p) for p in w.projections], [w] * len(w.projections)
 
 
+def _random_slices(i):
+    """Seeded random slice set: 2-4 projections of one input (own output
+    width, rank capacity, ranks and scales each), bf16 or fp8 base."""
+    g = np.random.default_rng(8100 + i)
+    base = "fp8" if i % 2 else "bf16"
+    T = int(g.integers(1, 1200))
+    d_in = int(64 * g.integers(1, 20)) if i % 3 else int(16 * g.integers(1, 80))
+    N = int(g.integers(1, 200))
+    ids = np.minimum(g.zipf(1.2, T) - 1, N - 1) if g.uniform() < 0.5 else g.integers(0, N, T)
+    ids = np.where(g.uniform(size=T) < 0.1, -1, ids).astype(np.int32)
+    active = (g.uniform(size=T) > 0.1).astype(np.uint8)
+    from lora_inputs import Projection, Workload
+    projs = []
+    for k in range(int(g.integers(2, 5))):
+        r_cap = int(g.choice([8, 16, 32, 64]))
+        ranks = np.where(g.uniform(size=N) < 0.3, r_cap, g.integers(1, r_cap + 1, N)).astype(np.int32)
+        projs.append(Projection(f"s{k}", d_in, int(8 * g.integers(1, 700)), N, r_cap, ranks,
+                                g.uniform(0.25, 2.0, N).astype(np.float32), 0.05, 0.05, 0.05, base, "bf16",
+                                (i, 88, k)))
+    return Workload("random_slices", i, T, projs, ids, active, "bf16")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_slices_parity(i):
+    """Seeded random slice sets in one launch: every slice against the fp64
+    oracle (W8A8 against its quantised definition) and the base products
+    alone against the oracle without adapters."""
+    w = _random_slices(i)
+    dps = [DevProjection(w, p) for p in w.projections]
+    p0 = dps[0].p
+    print(f"case {i}: {p0.base_dtype} T={w.T} d_in={p0.d_in} slices {[(d.p.d_out, d.p.r_cap) for d in dps]} "
+          f"N={p0.n_slots}", flush=True)
+    seg, s = segments(w, p0.n_slots)
+    x, x_host = dps[0].x, dps[0].x_host
+    bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3}[p0.base_dtype]
+    vs = []
+    for dp in dps:
+        v = torch.zeros(w.T, dp.p.r_cap, device=DEV)
+        agm.shrink(dp.pool, seg, w.T, s, x, v)
+        vs.append(v)
+    d_outs = [dp.p.d_out for dp in dps]
+    for flags in ([0, agm.FLAG_ACT_QUANT_E4M3] if p0.base_dtype == "fp8" else [0]):
+        wsp = agm.fused_slices_workspace(w.T, p0.d_in, d_outs, bt, flags, device=DEV)
+        ys = [torch.full((w.T, dp.p.d_out), float("nan"), device=DEV).to(dp.ydtype) for dp in dps]
+        agm.fused_linear_slices([dp.base for dp in dps], [dp.pool for dp in dps], seg, x, vs, ys, flags=flags,
+                                workspace=wsp)
+        torch.cuda.synchronize()
+        for dp, y in zip(dps, ys):
+            got = to_f64(y)
+            args = dp.oracle_args(w)[1:]
+            if flags:
+                ref, tol = oracle.linear_w8a8(x_host, dp.w0_host[0], dp.w0_host[1], *args), TOL["bf16"]
+            else:
+                ref, tol = oracle.linear(x_host, dp.w0_host, *args), _tol(dp.p)
+            assert rel_l2(got, ref) <= tol and row_rel_l2(got, ref) <= tol, (i, dp.p.name, flags)
+    ys = [torch.full((w.T, dp.p.d_out), float("nan"), device=DEV).to(dp.ydtype) for dp in dps]
+    wsp = agm.fused_slices_workspace(w.T, p0.d_in, d_outs, bt, 0, device=DEV)
+    agm.fused_linear_slices([dp.base for dp in dps], None, seg, x, None, ys, workspace=wsp)
+    torch.cuda.synchronize()
+    no_ids = np.full(w.T, -1, np.int32)
+    for dp, y in zip(dps, ys):
+        ref = oracle.linear(x_host, dp.w0_host, no_ids, w.active, dp.A_host, dp.B_host, dp.p.slot_rank,
+                            dp.p.slot_scale)
+        assert rel_l2(to_f64(y), ref) <= _tol(dp.p)
+
+
 @pytest.mark.parametrize("case", list(SLICES))
 def test_fused_slices_parity(case):
     w, dps, ws = _slice_setup(case)
