@@ -1084,6 +1084,79 @@ def test_random_shapes_segments_shrink_expand(i):
     assert np.all(d_got[~live] == 0)
 
 
+def _random_decode(i, kinds):
+    """Seeded small-batch case (T <= 256, <= 1024 slots) for the one-launch
+    build + shrink and the in-launch shrink."""
+    g = np.random.default_rng(9100 + i)
+    kind = kinds[i % len(kinds)]
+    dtype = "fp32" if kind == "fp32" else "bf16"
+    T = int(g.integers(1, 257))
+    d_in = int(64 * g.integers(1, 40))
+    d_out = int(8 * g.integers(1, 400))
+    N = int(g.integers(1, 1025))
+    r_cap = int(g.choice([8, 16, 32, 64]))
+    ranks = np.where(g.uniform(size=N) < 0.3, r_cap, g.integers(1, r_cap + 1, N)).astype(np.int32)
+    ids = np.minimum(g.zipf(1.1, T) - 1, N - 1) if g.uniform() < 0.5 else g.integers(0, N, T)
+    ids = np.where(g.uniform(size=T) < 0.2, -1, ids).astype(np.int32)
+    active = (g.uniform(size=T) > 0.25).astype(np.uint8)
+    from lora_inputs import Projection, Workload
+    base = "fp8" if kind == "fp8" else dtype
+    proj = Projection("p", d_in, d_out, N, r_cap, ranks, g.uniform(0.25, 2.0, N).astype(np.float32),
+                      0.05, 0.05, 0.05, base, dtype, (i, 99))
+    return kind, Workload("random_decode", i, T, [proj], ids, active, dtype)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_build_shrink(i):
+    """Seeded small batches through the one-launch build + shrink: its segment
+    buffer equals the device builder's bit for bit, and its v the oracle's."""
+    kind, w = _random_decode(i, ["bf16", "fp32"])
+    p = w.projections[0]
+    print(f"case {i}: {kind} T={w.T} d_in={p.d_in} N={p.n_slots} r_cap={p.r_cap}", flush=True)
+    dp = DevProjection(w, p)
+    ids = torch.from_numpy(w.ids).to(DEV)
+    act = torch.from_numpy(w.active).to(DEV)
+    order = i % 2
+    seg_ref = torch.full((agm.segment_words(w.T),), -7, dtype=torch.int32, device=DEV)
+    agm.build_segments_dev(ids, act, p.n_slots, seg_ref, order)
+    seg = torch.full((agm.segment_words(w.T),), -9, dtype=torch.int32, device=DEV)
+    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)
+    agm.build_shrink_dev(ids, act, dp.pool, seg, dp.x, v, order=order)
+    torch.cuda.synchronize()
+    d_ref, d = split_seg(seg_ref, w.T), split_seg(seg, w.T)
+    words = d_ref["sum"]
+    assert int(words[7]) == 0 and np.array_equal(d["sum"][:8], words[:8])
+    for a, b in zip(_seg_meaningful(d, words), _seg_meaningful(d_ref, words)):
+        assert np.array_equal(a, b)
+    n = int(words[0])
+    if n:
+        mask = np.arange(p.r_cap)[None, :] < p.slot_rank[w.ids[d_ref["perm"][:n]]][:, None]
+        vg = v.cpu().numpy()[:n].astype(np.float64)
+        assert rel_l2(np.where(mask, vg, 0.0), _v_ref(dp, w, d_ref)) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_shrink_in_launch(i):
+    """Seeded small batches through the fused call that computes its shrink in
+    the same launch (bf16 and widened fp8): v and y against the oracle."""
+    kind, w = _random_decode(i, ["bf16", "fp8"])
+    p = w.projections[0]
+    print(f"case {i}: {kind} T={w.T} {p.d_in}->{p.d_out} N={p.n_slots} r_cap={p.r_cap}", flush=True)
+    dp = DevProjection(w, p)
+    seg, s = segments(w, p.n_slots)
+    y, v = _fused_in_launch(dp, seg, w)
+    segd = split_seg(seg, w.T)
+    n = s.n_active
+    if n:
+        rk = p.slot_rank[segd["seg_adapter"][segd["pos_seg"][:n]]]
+        mask = np.arange(p.r_cap)[None, :] < rk[:, None]
+        assert rel_l2(v[:n][mask], _v_ref(dp, w, segd)[mask]) <= TOL["fp32"]
+    ref = oracle.linear(dp.x_host, dp.w0_host, *dp.oracle_args(w)[1:])
+    tol = _tol(p)
+    assert np.isfinite(y).all()
+    assert rel_l2(y, ref) <= tol and row_rel_l2(y, ref) <= tol
+
+
 @pytest.mark.parametrize("T,d_out", [(512, 9216),    # persistent 128 x 128 W8A16 tiles
                                      (256, 264),     # 64 x 64 W8A16 tiles
                                      (528, 1000)])   # d_in % 64 != 0: the general kernel
