@@ -2,8 +2,9 @@
 // adapter segment ("LoRazor" 3.1.1 Eq. 1; "LoRAForge" 5, rank-aware shrink:
 // directions beyond the adapter's retained rank exit before reading operands).
 //
-// bf16 pools: one work item is (row tile of <= 16 rows of one segment, NB
-// consecutive blocks of db = 16, 8 or 4 rank directions), each block computed
+// bf16 pools: one work item is (row tile of <= 16 rows of one segment, or
+// one half of it in batches of at most 256 rows, NB consecutive blocks of
+// db = 16, 8 or 4 rank directions), each block computed
 // as a 16 x 16 tile of MFMA v_mfma_f32_16x16x32_bf16 products that share the
 // item's x fragments.  Small batches use narrow blocks and one block per
 // item, so that enough workgroups share the A rows to keep the chip's CUs
@@ -116,15 +117,21 @@ ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, 
   if ((long)T >= 8 * bound)
     while (nb < 8 && nb < nblocks && bound * ((nblocks + 2 * nb - 1) / (2 * nb)) >= kMinItems) nb *= 2;
   a.nrb = (nblocks + nb - 1) / nb;
+  // batches of at most 256 rows split every row tile into two items of up to
+  // 8 rows: the few full tiles of a batch of mostly one-row tiles (a Zipf head
+  // adapter) then stream half the x bytes each, which is where such a launch
+  // waits longest (measured: the decode batch's build + shrink 11.3 -> 10.3
+  // us; four parts, or halves for longer batches, are slower)
+  a.rsub = T <= kSmallRows ? 2 : 1;
   // row tiles: the bound for PERSISTENT, else the mode's host count
   const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT ? bound : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
   ShrinkShape sh;
   sh.nb = nb;
   if (ls.mode == LORA_LAUNCH_PERSISTENT) {
     a.n_items = 0;
-    sh.grid = (int)std::min<long>(tiles * a.nrb, max_grid);
+    sh.grid = (int)std::min<long>(tiles * a.nrb * a.rsub, max_grid);
   } else {
-    a.n_items = (int)(tiles * a.nrb);
+    a.n_items = (int)(tiles * a.nrb * a.rsub);
     // (at least one workgroup, which finds the device's own count)
     sh.grid = std::max(a.n_items, 1);
   }

@@ -22,6 +22,7 @@ struct ShrinkArgs {
   int ld_x, r_cap, d_in, T, ld_v;
   int mode, db, nrb, rtiles, n_items;  // nrb: items per row tile; n_items: host item count (FULL_BATCH)
   int slots;                           // L = min(T, n_slots) adapter slots (BUCKETED)
+  int rsub = 1;                        // items per row tile and rank block (row halves: 2)
 };
 
 constexpr int kUnroll = 8;        // k chunks in flight per wave
@@ -43,14 +44,15 @@ __device__ __forceinline__ f32x4_t mfma_chunk(const u32x4_t& xv, const u32x4_t& 
   }
 }
 
-// One item: row tile w (first grouped position and segment) and its rb-th
+// One item: row tile w (first grouped position and segment), its sub-th part
+// of LORA_TILE_SMALL / a.rsub rows (empty parts return at once) and its rb-th
 // group of NB rank blocks, by a workgroup of WAVES waves; red is LDS of
 // WAVES x 64 x 16 bytes.  COH: v is stored device-coherently (scope sc1:
 // never left dirty in, nor read stale from, one XCD's L2), for a consumer in
 // the same launch that reads it after a counter says it is complete.
 template <typename TI, int NB, int WAVES, bool COH = false>
 __device__ __forceinline__ void shrink_item_body(const ShrinkArgs& a, const SegPtrs& P, TileWork w, int rb,
-                                                 f32x4_t (*red)[64]) {
+                                                 f32x4_t (*red)[64], int sub = 0) {
   constexpr int VEC = 16 / sizeof(TI);      // elements per 16-byte load
   constexpr int KC = 4 * VEC;               // k per chunk (4 lane groups)
   constexpr int UNR = kUnroll / NB > 0 ? kUnroll / NB : 1;   // k chunks in flight per wave
@@ -63,7 +65,8 @@ __device__ __forceinline__ void shrink_item_body(const ShrinkArgs& a, const SegP
     // (the item is the workgroup's: its tile record is wave-uniform, and so
     // are the segment's end, adapter and rank read from it, which steer
     // branches around barriers)
-    w.p0 = __builtin_amdgcn_readfirstlane(w.p0);
+    const int sub_rows = LORA_TILE_SMALL / a.rsub;
+    w.p0 = __builtin_amdgcn_readfirstlane(w.p0) + sub * sub_rows;
     w.seg = __builtin_amdgcn_readfirstlane(w.seg);
     // segment end, adapter and the tile's 16 permutation entries (row frow,
     // or a later valid row past the tile) as one round of loads
@@ -73,7 +76,8 @@ __device__ __forceinline__ void shrink_item_body(const ShrinkArgs& a, const SegP
     // an empty use of all three keeps the compiler from sinking the segment
     // end and the permutation loads past the rank test below
     asm volatile("" ::"v"(seg_end), "v"(adapter), "v"(my_perm));
-    w.rows = min(LORA_TILE_SMALL, seg_end - w.p0);
+    w.rows = min(sub_rows, seg_end - w.p0);
+    if (w.rows <= 0) return;                 // a part past the segment's rows
     const int r = __builtin_amdgcn_readfirstlane(a.slot_rank[adapter]);
     const int j0 = rb * NB * a.db;
     if (j0 >= r) return;                     // directions beyond the retained rank
@@ -158,7 +162,8 @@ __device__ __forceinline__ void shrink_items(const ShrinkArgs& a, const SegPtrs&
   // with the permutation entries of all 16 rows the tile may hold.
   // (all five loads before any branch; the tile index is clamped into the
   // list's T entries, T >= 1 for every launch)
-  const int first_tile = min((int)(blockIdx.x / a.nrb), a.T - 1);
+  const int ipt = a.nrb * a.rsub;       // items per row tile
+  const int first_tile = min((int)(blockIdx.x / ipt), a.T - 1);
   int rec_p0 = P.tiles_small[2 * first_tile];
   int rec_seg = P.tiles_small[2 * first_tile + 1];
   const int n_tiles = P.sum[kNTilesSmall];
@@ -172,15 +177,16 @@ __device__ __forceinline__ void shrink_items(const ShrinkArgs& a, const SegPtrs&
   // a summary of another batch costs time, never rows.
   int n_items = a.n_items, rtiles = a.rtiles;
   if (listed) {
-    n_items = n_tiles * a.nrb;
+    n_items = n_tiles * ipt;
   } else if (a.mode == LORA_LAUNCH_BUCKETED) {
     rtiles = (P.sum[kRowBound] + LORA_TILE_SMALL - 1) / LORA_TILE_SMALL;
-    n_items = a.slots * rtiles * a.nrb;
+    n_items = a.slots * rtiles * ipt;
   }
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile_item = item / a.nrb;
-    const int rb = item - tile_item * a.nrb;
+    const int tile_item = item / ipt;
+    const int in_tile = item - tile_item * ipt, sub = in_tile / a.nrb;
+    const int rb = in_tile - sub * a.nrb;
     TileWork w;
     if (listed) {
       if (tile_item >= n_tiles) continue;   // a host count that disagrees with the device buffer
@@ -193,7 +199,7 @@ __device__ __forceinline__ void shrink_items(const ShrinkArgs& a, const SegPtrs&
     } else if (!decode_tile<LORA_TILE_SMALL>(P, a.mode, tile_item, P.tiles_small, rtiles, w)) {
       continue;
     }
-    shrink_item_body<TI, NB, WAVES>(a, P, w, rb, red);
+    shrink_item_body<TI, NB, WAVES>(a, P, w, rb, red, sub);
   }
 }
 
