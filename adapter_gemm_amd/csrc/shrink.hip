@@ -3,7 +3,7 @@
 // directions beyond the adapter's retained rank exit before reading operands).
 //
 // bf16 pools: one work item is (row tile of <= 16 rows of one segment, or
-// one half of it in batches of at most 256 rows, NB consecutive blocks of
+// one half of it in the one-launch build + shrink, NB consecutive blocks of
 // db = 16, 8 or 4 rank directions), each block computed
 // as a 16 x 16 tile of MFMA v_mfma_f32_16x16x32_bf16 products that share the
 // item's x fragments.  Small batches use narrow blocks and one block per
@@ -92,7 +92,8 @@ struct ShrinkShape {
   int nb, grid;
 };
 
-ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, ShrinkArgs& a, int max_grid) {
+ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, ShrinkArgs& a, int max_grid,
+                         int rsub = 1) {
   a.A = pool.A;
   a.slot_rank = pool.slot_rank;
   a.r_cap = pool.r_cap;
@@ -117,12 +118,7 @@ ShrinkShape shrink_shape(const lora_pool_t& pool, int T, const LaunchShape& ls, 
   if ((long)T >= 8 * bound)
     while (nb < 8 && nb < nblocks && bound * ((nblocks + 2 * nb - 1) / (2 * nb)) >= kMinItems) nb *= 2;
   a.nrb = (nblocks + nb - 1) / nb;
-  // batches of at most 256 rows split every row tile into two items of up to
-  // 8 rows: the few full tiles of a batch of mostly one-row tiles (a Zipf head
-  // adapter) then stream half the x bytes each, which is where such a launch
-  // waits longest (measured: the decode batch's build + shrink 11.3 -> 10.3
-  // us; four parts, or halves for longer batches, are slower)
-  a.rsub = T <= kSmallRows ? 2 : 1;
+  a.rsub = rsub;
   // row tiles: the bound for PERSISTENT, else the mode's host count
   const long tiles = ls.mode == LORA_LAUNCH_PERSISTENT ? bound : (long)host_tile_items(ls, T, LORA_TILE_SMALL);
   ShrinkShape sh;
@@ -189,8 +185,13 @@ hipError_t launch_build_shrink(const int32_t* ids, const uint8_t* active, int T,
   a.ld_v = ld_v;
   LaunchShape ls{LORA_LAUNCH_PERSISTENT, 0, 0, std::min(T, pool.n_slots)};
   // every workgroup builds the segments, so the grid is the item bound (at
-  // least one workgroup, which writes the segment buffer)
-  const ShrinkShape sh = shrink_shape(pool, T, ls, a, 1 << 20);
+  // least one workgroup, which writes the segment buffer).  Every row tile
+  // is split into two items of up to 8 rows: the few full tiles of a batch of
+  // mostly one-row tiles (a Zipf head adapter) then stream half the x bytes
+  // each, which is where this launch waits longest (measured: the decode
+  // batch 11.3 -> 10.3 us; four parts slower, and in the separate shrink of
+  // 1024-thread workgroups the doubled item count costs more than it saves)
+  const ShrinkShape sh = shrink_shape(pool, T, ls, a, 1 << 20, 2);
   const int grid = std::max(sh.grid, 1);
   const size_t lds = small_build_lds_bytes(pool.n_slots);
   with_nb(sh.nb, [&](auto nb_c) {
