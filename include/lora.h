@@ -468,6 +468,10 @@ int lora_stream_destroy(void* stream);
  *   q[i, k] = e4m3( x[i, k] / s_x[i] ), fp32 division, round to nearest
  *             even, saturating to +-448
  *   x  device bf16 [T, ld_x]; q device uint8 [T, ld_q]; s_x device fp32 [T]
+ * Rows must be finite: a NaN or an infinity leaves its row's codes and s_x
+ * unspecified.  Errors (checked before any launch): LORA_E_ARG for negative
+ * sizes, NULL pointers with T > 0, or ld_x / ld_q < d; LORA_E_ALIGN unless
+ * d % 16 == 0, ld_x % 8 == 0, ld_q % 16 == 0 and x and q are 16-byte aligned.
  */
 int lora_quantize_e4m3(const void* x, int32_t T, int32_t d, int32_t ld_x, uint8_t* q, int32_t ld_q,
                        float* s_x, void* stream);

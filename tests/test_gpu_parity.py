@@ -758,6 +758,47 @@ def test_fused_w8a8_parity():
     assert rel_l2(y, ref8) <= TOL["bf16"]
 
 
+# every amax is a bf16 value: s_x = 3, 5, 1, inexact ones (312, 7.5, 0.1, 30720),
+# a small one, 2^-90 and its neighbours on either side (1.5 and 1.75 x 2^-82,
+# 2^-80), a huge one (2^103) and a subnormal one
+_QUANT_AMAX = [1344.0, 2240.0, 448.0, 312.0, 7.5, 0.10009765625, 30720.0, 0.0478515625,
+               1.5 * 2.0 ** -82, 1.75 * 2.0 ** -82, 2.0 ** -80, 2.0 ** 103, 1.1663108e-38]
+
+
+@pytest.mark.parametrize("d", [5136, 17424])
+@pytest.mark.parametrize("amax", _QUANT_AMAX)
+def test_quantize_e4m3_every_bf16_value(amax, d):
+    """Every finite bf16 value of magnitude <= amax, over rows of d values that
+    each end in amax (so that every row's s_x = amax / 448 exactly as chosen),
+    against the oracle's codes bit for bit: every quotient a row can produce,
+    ties and near-ties to the e4m3 rounding boundaries included.  d: a row of
+    up to 16384 values (held in registers between the two passes, here with a
+    ragged last 2048-value chunk) and a longer one."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= np.float32(amax))]
+    per = d - 1
+    T = -(-len(vals) // per)
+    flat = np.zeros(T * per, np.float32)    # (the padding is zeros)
+    flat[:len(vals)] = vals
+    x = np.empty((T, d), np.float32)
+    x[:, :per] = flat.reshape(T, per)
+    x[:, -1] = amax
+    from lora_inputs import bf16_round
+    assert np.array_equal(bf16_round(x).view(np.uint16).astype(np.uint32) << 16, x.view(np.uint32))
+    xd = bf16_dev(bf16_round(x))
+    q = torch.empty(T, d, dtype=torch.uint8, device=DEV)
+    s = torch.empty(T, dtype=torch.float32, device=DEV)
+    agm.quantize_e4m3(xd, q, s)
+    torch.cuda.synchronize()
+    codes, sx = oracle.act_quant_e4m3(x)
+    assert np.array_equal(s.cpu().numpy(), sx)
+    got = q.cpu().numpy()
+    bad = np.argwhere(got != codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first (x, got, want): " + ", ".join(
+        f"({x[i, k]!r}, {got[i, k]:#04x}, {codes[i, k]:#04x})" for i, k in bad[:12])
+
+
 def test_quantize_e4m3_bit_exact():
     g = np.random.default_rng(0)
     from lora_inputs import bf16_round
