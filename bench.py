@@ -452,6 +452,34 @@ def fused_path(S: Setup, steps: int, warmup: int, flags: int, slices: bool, sepa
     }
 
 
+def quant_roofline(S: Setup, steps: int, warmup: int):
+    """The W8A8 activation quantisation alone (lora_quantize_e4m3 on the
+    workload's x), against the HBM roofline: T*d bf16 read, T*d codes and T
+    scales written per launch; an event pair around every launch on the
+    stream the library launches on."""
+    import torch
+    agm = S.agm
+    x = S.insts[0]["inst"][0]["x"]
+    T, d = int(x.shape[0]), int(x.shape[1])
+    q = torch.empty(T, d, dtype=torch.uint8, device=x.device)
+    s = torch.empty(T, dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        agm.quantize_e4m3(x, q, s)
+    torch.cuda.synchronize()
+    evs = [ev_pair() for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        agm.quantize_e4m3(x, q, s)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps * 1e3
+    nbytes = T * d * 2 + T * d + 4 * T
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "quant_kernel", "shape": [T, d], "us_per_launch": round(us, 2), "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+
+
 def unfused_adapter(S: Setup, steps: int, warmup: int, modes):
     """The adapter term without fusion: lora_shrink then lora_expand (y += s B v
     in place) for every projection, per launch-sizing mode ("LoRazor" 3.1.1-3.1.2:
@@ -620,6 +648,7 @@ def main():
         if name == "fp8_fused":
             per_cfg["fp8_fused_w8a8"] = _cfg_entry(fused_path(Sc, steps_c, warm_c, agm.FLAG_ACT_QUANT_E4M3, True,
                                                               args.separate_build))
+            per_cfg["fp8_fused_w8a8"]["quant_hbm"] = quant_roofline(Sc, steps_c, warm_c)
         if name in ("decode_bgmv", "fp8_fused"):
             # the shrink inside the fused launch, against the separate launches above
             per_cfg[name + "_shrink_in_launch"] = _cfg_entry(
