@@ -366,11 +366,16 @@ struct F32Args {
 };
 
 constexpr int kF32Tile = 32;
+constexpr int kF32Pre = 8;    // k blocks of 64 whose loads are in flight at once
 
 __global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
-  constexpr int BM = kF32Tile, BN = kF32Tile, BK = 64;
-  __shared__ float As[BK][BM + 1];
-  __shared__ float Ws[BK][BN + 1];
+  // k goes in chunks of KC = kF32Pre x 64: all of a chunk's loads go out at
+  // once (a 64-wide block's FMAs take far less than one memory round trip,
+  // so loading one block ahead would leave each block waiting for its own
+  // loads), then the chunk is staged in LDS and multiplied in one loop
+  constexpr int BM = kF32Tile, BN = kF32Tile, BK = 64, KC = kF32Pre * BK;
+  __shared__ float As[KC][BM + 1];
+  __shared__ float Ws[KC][BN + 1];
   const int tid = threadIdx.x;
   const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -381,41 +386,52 @@ __global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
     has_seg = seg_valid(P, a.T);
   }
 
-  // staging: row lr of the tile, 8 consecutive k (d_in, ld_x, ld_w are
-  // multiples of 8 and the rows 16-byte aligned: two float4 loads, all in or
-  // all out of range)
+  // staging: row lr of the tile, 8 consecutive k of each 64-wide block
+  // (d_in, ld_x, ld_w are multiples of 8 and the rows 16-byte aligned: two
+  // float4 loads, all in or all out of range).  Every load goes out
+  // unconditionally, from row 0 or the row's last 8 values where the tile's
+  // row or k is past the operand, and such values become zeros only when
+  // staged: a load under a per-lane branch, or a select right after it,
+  // would be waited for at once.
   const int lr = tid >> 3, lk = (tid & 7) * 8;
   const int apos = m0 + lr;
   const float* xrow = nullptr;
   if (apos < a.T) xrow = a.x + (size_t)(has_seg ? P.perm[apos] : apos) * a.ld_x;
   const float* wrow = (n0 + lr < a.d_out) ? a.W + (size_t)(n0 + lr) * a.ld_w : nullptr;
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t xa[2], wa[2];
-  auto load = [&](int k0) {
-    const int k = k0 + lk;
-    const bool in = k < a.d_in;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      xa[h] = (xrow && in) ? *reinterpret_cast<const f32x4_t*>(xrow + k + 4 * h) : zero;
-      wa[h] = (wrow && in) ? *reinterpret_cast<const f32x4_t*>(wrow + k + 4 * h) : zero;
-    }
-  };
+  const float* xsrc = xrow ? xrow : a.x;
+  const float* wsrc = wrow ? wrow : a.W;
+  f32x4_t xa[kF32Pre][2], wa[kF32Pre][2];
 
   const int ty = tid >> 4, tx = tid & 15;
   float acc[2][2] = {};
-  load(0);
-  for (int k0 = 0; k0 < a.d_in; k0 += BK) {
+  for (int c0 = 0; c0 < a.d_in; c0 += KC) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int p = 0; p < kF32Pre; ++p) {
+      const int k = c0 + p * BK + lk;
+      const int kc = k < a.d_in ? k : a.d_in - 8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        As[lk + 4 * h + e][lr] = xa[h][e];
-        Ws[lk + 4 * h + e][lr] = wa[h][e];
+      for (int h = 0; h < 2; ++h) {
+        xa[p][h] = *reinterpret_cast<const f32x4_t*>(xsrc + kc + 4 * h);
+        wa[p][h] = *reinterpret_cast<const f32x4_t*>(wsrc + kc + 4 * h);
       }
+    }
+    if (c0 > 0) __syncthreads();              // every wave is done with the previous chunk
+#pragma unroll
+    for (int p = 0; p < kF32Pre; ++p) {
+      const bool in = c0 + p * BK + lk < a.d_in;
+      const bool xin = xrow && in, win = wrow && in;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          As[p * BK + lk + 4 * h + e][lr] = xin ? xa[p][h][e] : 0.f;
+          Ws[p * BK + lk + 4 * h + e][lr] = win ? wa[p][h][e] : 0.f;
+        }
+    }
     __syncthreads();
-    if (k0 + BK < a.d_in) load(k0 + BK);      // the next block's loads overlap these FMAs
-#pragma unroll 16
-    for (int kk = 0; kk < BK; ++kk) {
+    const int kn = min(KC, a.d_in - c0);      // a multiple of 8
+#pragma unroll 8
+    for (int kk = 0; kk < kn; ++kk) {
       const float a0 = As[kk][ty * 2], a1 = As[kk][ty * 2 + 1];
       const float w0 = Ws[kk][tx * 2], w1 = Ws[kk][tx * 2 + 1];
       acc[0][0] = fmaf(a0, w0, acc[0][0]);
@@ -423,35 +439,87 @@ __global__ __launch_bounds__(256) void fused_f32_kernel(F32Args a) {
       acc[1][0] = fmaf(a1, w0, acc[1][0]);
       acc[1][1] = fmaf(a1, w1, acc[1][1]);
     }
-    __syncthreads();
   }
 
+  // Epilogue: y[row, n] = acc + s_a sum_j v[pos, j] B_a[n, j] for live rows.
+  // The loads go out one round per link of the chain (permutation and
+  // segment -> adapter -> rank and scale -> v and B), for both of the
+  // thread's rows at once, from indices clamped into their arrays; values of
+  // rows past T or not live are never used.
   const int n_active = (has_seg && a.B) ? P.sum[kNActive] : 0;
+  int pos[2], row[2], ad[2] = {0, 0}, rk[2] = {0, 0};
+  bool live[2];
+  float sc[2] = {0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int pos = m0 + ty * 2 + i;
-    if (pos >= a.T) continue;
-    const int row = has_seg ? P.perm[pos] : pos;
-    int ad = -1, r = 0;
-    float sc = 0.f;
-    if (pos < n_active) {
-      ad = P.seg_adapter[P.pos_seg[pos]];
-      r = a.slot_rank[ad];
-      sc = a.slot_scale[ad];
+    pos[i] = m0 + ty * 2 + i;
+    live[i] = pos[i] < n_active;                // (n_active <= T; 0 without a pool or segments)
+  }
+  if (has_seg) {
+    int sg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pc = min(pos[i], a.T - 1);
+      row[i] = P.perm[pc];
+      sg[i] = P.pos_seg[pc];
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ad[i] = P.seg_adapter[min(max(sg[i], 0), a.T - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) row[i] = pos[i];
+  }
+  if (live[0] || live[1]) {
+    // (a row that is not live takes the other row's adapter: a valid slot)
+    const int s0 = live[0] ? ad[0] : ad[1], s1 = live[1] ? ad[1] : ad[0];
+    const int r0 = a.slot_rank[s0], r1 = a.slot_rank[s1];
+    const float c0 = a.slot_scale[s0], c1 = a.slot_scale[s1];
+    ad[0] = s0;
+    ad[1] = s1;
+    rk[0] = live[0] ? min(r0, a.r_cap) : 0;
+    rk[1] = live[1] ? min(r1, a.r_cap) : 0;
+    sc[0] = c0;
+    sc[1] = c1;
+  }
+  // ranks in batches of 16: every v and B load of a batch goes out before
+  // its FMAs; ranks at or past a row's rank are dropped (v may hold anything
+  // there)
+  float dot[2][2] = {};
+  const int nbat = (max(rk[0], rk[1]) + 15) / 16;
+  for (int bt = 0; bt < nbat; ++bt) {
+    const int j0 = bt * 16;
+    f32x4_t vv[2][4], bb[2][2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float* vr = a.v + (size_t)min(pos[i], a.T - 1) * a.ld_v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vv[i][q] = *reinterpret_cast<const f32x4_t*>(vr + min(j0 + 4 * q, a.r_cap - 4));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = min(n0 + tx * 2 + j, a.d_out - 1);
+        const float* br = a.B + ((size_t)ad[i] * a.d_out + n) * a.r_cap;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bb[i][j][q] = *reinterpret_cast<const f32x4_t*>(br + min(j0 + 4 * q, a.r_cap - 4));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + 4 * q + e < rk[i]) dot[i][j] = fmaf(vv[i][q][e], bb[i][j][q][e], dot[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (pos[i] >= a.T) continue;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + tx * 2 + j;
       if (n >= a.d_out) continue;
-      float out = acc[i][j];
-      if (ad >= 0) {
-        const float* vr = a.v + (size_t)pos * a.ld_v;
-        const float* br = a.B + ((size_t)ad * a.d_out + n) * a.r_cap;
-        float d = 0.f;
-        for (int jj = 0; jj < r; ++jj) d = fmaf(vr[jj], br[jj], d);
-        out = fmaf(sc, d, out);
-      }
-      a.y[(size_t)row * a.ld_y + n] = out;
+      a.y[(size_t)row[i] * a.ld_y + n] = rk[i] > 0 ? fmaf(sc[i], dot[i][j], acc[i][j]) : acc[i][j];
     }
   }
 }
