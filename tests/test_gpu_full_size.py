@@ -161,3 +161,66 @@ def test_full_size_bench_path(name):
         print(f"[full-size] {name}/{p.name}: rel L2 {rel_l2(got, y_ref):.2e} on {len(sel)} rows", flush=True)
         del dp, v, y
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["decode_bgmv", "fp8_fused"])
+def test_full_size_shrink_in_launch(name):
+    """The configuration bench.py times as `<workload>_shrink_in_launch`: the
+    device segment build, then one fused call that computes v in the same
+    launch (W8A16 for the fp8 base); v and y on sampled rows against the
+    oracle."""
+    w = make_workload(name)
+    p = w.projections[0]
+    print(f"[full-size] {name} (shrink in the fused launch): T={w.T}", flush=True)
+    ids = torch.from_numpy(w.ids.astype(np.int32)).to(DEV)
+    act = torch.from_numpy(w.active.astype(np.uint8)).to(DEV)
+    seg = torch.empty(agm.segment_words(w.T), dtype=torch.int32, device=DEV)
+    agm.build_segments_dev(ids, act, p.n_slots, seg)
+    dp = DevProjection(w, p)
+    v = torch.full((w.T, p.r_cap), float("nan"), device=DEV)     # an output of the call
+    y = torch.full((w.T, p.d_out), float("nan"), device=DEV).to(dp.ydtype)
+    bt = {"bf16": agm.BF16, "fp8": agm.FP8_E4M3}[p.base_dtype]
+    ws = agm.fused_workspace(w.T, p.d_in, p.d_out, bt, agm.FLAG_SHRINK_IN_LAUNCH, device=DEV)
+    agm.fused_linear(dp.base, dp.pool, seg, dp.x, v, y, flags=agm.FLAG_SHRINK_IN_LAUNCH, workspace=ws)
+    torch.cuda.synchronize()
+    d = split_seg(seg, w.T)
+    assert int(d["sum"][7]) == 0
+    pos_of_row = np.empty(w.T, np.int64)
+    pos_of_row[d["perm"]] = np.arange(w.T)
+    n_act = int(d["sum"][0])
+    sel = _sample_rows(w)
+    xs = dp.x_host[sel]
+    ids_s, act_s = w.ids[sel], w.active[sel]
+    args = dp.oracle_args(w)
+    y_ref = oracle.linear(xs, dp.w0_host, ids_s, act_s, *args[3:])
+    got = to_f64(y)[sel]
+    tol = TOL["fp8"] if p.base_dtype == "fp8" else TOL[p.data_dtype]
+    assert np.isfinite(got).all(), name
+    assert rel_l2(got, y_ref) <= tol and row_rel_l2(got, y_ref) <= tol, (name, rel_l2(got, y_ref))
+    live_s = oracle.live_rows(ids_s, act_s)
+    if live_s.any():
+        v_ref = oracle.shrink_rows(xs[live_s], ids_s[live_s], act_s[live_s], dp.A_host, p.slot_rank)
+        pos = pos_of_row[sel[live_s]]
+        assert (pos < n_act).all()
+        vg = v.cpu().numpy().astype(np.float64)[pos]
+        mask = np.arange(p.r_cap)[None, :] < p.slot_rank[ids_s[live_s]][:, None]
+        assert rel_l2(np.where(mask, vg, 0), v_ref) <= TOL["fp32"], name
+    print(f"[full-size] {name} (shrink in the fused launch): rel L2 {rel_l2(got, y_ref):.2e} on {len(sel)} rows",
+          flush=True)
+
+
+def test_full_size_quantize_e4m3():
+    """The W8A8 activation quantisation on the fp8 workload's x (512 x 8192):
+    codes and s_x of sampled rows bit for bit against the oracle."""
+    w = make_workload("fp8_fused")
+    dp = DevProjection(w, w.projections[0])
+    T, d = dp.x.shape
+    q = torch.empty(T, d, dtype=torch.uint8, device=DEV)
+    s = torch.empty(T, dtype=torch.float32, device=DEV)
+    agm.quantize_e4m3(dp.x, q, s)
+    torch.cuda.synchronize()
+    sel = _sample_rows(w)
+    codes, sx = oracle.act_quant_e4m3(dp.x_host[sel])
+    assert np.array_equal(s.cpu().numpy()[sel], sx)
+    assert np.array_equal(q.cpu().numpy()[sel], codes)
+    print(f"[full-size] fp8_fused quantisation: {len(sel)} rows x {d} codes equal", flush=True)
