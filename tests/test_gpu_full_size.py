@@ -224,3 +224,47 @@ def test_full_size_quantize_e4m3():
     assert np.array_equal(s.cpu().numpy()[sel], sx)
     assert np.array_equal(q.cpu().numpy()[sel], codes)
     print(f"[full-size] fp8_fused quantisation: {len(sel)} rows x {d} codes equal", flush=True)
+
+
+@pytest.mark.parametrize("name", ["decode_bgmv", "llama_layer"])
+def test_full_size_unfused_shrink_expand(name):
+    """The unfused adapter term as bench.py times it (lora_shrink, then
+    lora_expand adding s B v into y in place) in every launch-sizing mode, on
+    the workload's first projection: y starts at zero, so it holds the adapter
+    term alone, checked on sampled rows against the oracle; the modes agree
+    bit for bit, and rows that are not live stay zero."""
+    w = make_workload(name)
+    p = w.projections[0]
+    dp = DevProjection(w, p)
+    T = w.T
+    seg = torch.empty(agm.segment_words(T), dtype=torch.int32, device=DEV)
+    staging = torch.empty(agm.segment_words(T), dtype=torch.int32).pin_memory()
+    summ = agm.build_segments(torch.from_numpy(w.ids.astype(np.int32)), torch.from_numpy(w.active.astype(np.uint8)),
+                              p.n_slots, seg, staging)
+    torch.cuda.synchronize()
+    modes = [agm.LAUNCH_EXACT, agm.LAUNCH_BUCKETED, agm.LAUNCH_FULL_BATCH]
+    if name == "decode_bgmv":
+        modes.insert(0, agm.LAUNCH_PERSISTENT)
+    sel = _sample_rows(w)
+    xs = dp.x_host[sel]
+    ids_s, act_s = w.ids[sel], w.active[sel]
+    live_s = oracle.live_rows(ids_s, act_s)
+    ref = oracle.lora_delta(xs, ids_s, act_s, dp.A_host, dp.B_host, p.slot_rank, p.slot_scale)
+    first = None
+    for mode in modes:
+        v = torch.zeros(T, p.r_cap, device=DEV)
+        y = torch.zeros(T, p.d_out, device=DEV).to(dp.ydtype)
+        agm.shrink(dp.pool, seg, T, summ, dp.x, v, launch=mode)
+        agm.expand(dp.pool, seg, T, summ, v, y, launch=mode)
+        torch.cuda.synchronize()
+        got = to_f64(y)[sel]
+        assert np.isfinite(got).all(), (name, mode)
+        assert not got[~live_s].any(), (name, mode)
+        assert rel_l2(got[live_s], ref[live_s]) <= TOL[p.data_dtype], (name, mode, rel_l2(got[live_s], ref[live_s]))
+        yb = y.view(torch.int16).cpu().numpy() if dp.ydtype == torch.bfloat16 else y.cpu().numpy()
+        if first is None:
+            first = yb
+        else:
+            assert np.array_equal(yb, first), (name, mode)
+        print(f"[full-size] {name}/{p.name} unfused, launch mode {mode}: adapter term rel L2 "
+              f"{rel_l2(got[live_s], ref[live_s]):.2e} on {int(live_s.sum())} live rows", flush=True)
