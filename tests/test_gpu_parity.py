@@ -587,7 +587,7 @@ def _random_slices(i):
     return Workload("random_slices", i, T, projs, ids, active, "bf16")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(16))
 def test_random_slices_parity(i):
     """Seeded random slice sets in one launch: every slice against the fp64
     oracle (W8A8 against its quantised definition) and the base products
@@ -1061,7 +1061,7 @@ def _random_case(i):
     return kind, w
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(48))
 def test_random_shapes_fused_parity(i):
     """A seeded sweep of shapes no other case pins down: every base type,
     T from one row up, ragged d_in / d_out, 1-299 slots, rank capacities 8-128
@@ -1088,7 +1088,7 @@ def test_random_shapes_fused_parity(i):
         assert rel_l2(y, ref8) <= TOL["bf16"] and row_rel_l2(y, ref8) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(32))
 def test_random_shapes_segments_shrink_expand(i):
     """The same seeded sweep through the other calls: the device builder's
     segment buffer bit-exact against the oracle's grouping (both orders), v of
@@ -1147,7 +1147,7 @@ def _random_decode(i, kinds):
     return kind, Workload("random_decode", i, T, [proj], ids, active, dtype)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(16))
 def test_random_build_shrink(i):
     """Seeded small batches through the one-launch build + shrink: its segment
     buffer equals the device builder's bit for bit, and its v the oracle's."""
@@ -1176,7 +1176,7 @@ def test_random_build_shrink(i):
         assert rel_l2(np.where(mask, vg, 0.0), _v_ref(dp, w, d_ref)) <= TOL["fp32"]
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(12))
 def test_random_shrink_in_launch(i):
     """Seeded small batches through the fused call that computes its shrink in
     the same launch (bf16 and widened fp8): v and y against the oracle."""
