@@ -20,9 +20,10 @@
 // slot s + P q reads row / direction s over the q-th of 16 / P k slices, so
 // no two lanes load the same bytes, and the slices' partial sums (the
 // diagonal P x P blocks of the product) are added in slice order.  The 16
-// waves of the workgroup take interleaved k chunks (so that for decode
-// widths every load of a wave is in flight at once) and their partial tiles
-// are summed through LDS in a fixed order: no atomics, bitwise reproducible.
+// waves of the workgroup (8 for bf16 items of four rank blocks, two
+// workgroups per CU) take interleaved k chunks (so that for decode widths
+// every load of a wave is in flight at once) and their partial tiles are
+// summed through LDS in a fixed order: no atomics, bitwise reproducible.
 //
 // fp32 pools use the same tiling with v_mfma_f32_16x16x4f32 (four MFMAs per
 // 16-byte load, one per element).
@@ -36,10 +37,10 @@
 namespace lora {
 namespace {
 
-template <typename TI, int NB>
-__global__ __launch_bounds__(kThreads) void shrink_mfma_kernel(ShrinkArgs a) {
-  __shared__ f32x4_t red[kWaves][64];
-  shrink_items<TI, NB, kWaves>(a, seg_ptrs(a.seg, a.T), red);
+template <typename TI, int NB, int WAVES = kWaves>
+__global__ __launch_bounds__(64 * WAVES) void shrink_mfma_kernel(ShrinkArgs a) {
+  __shared__ f32x4_t red[WAVES][64];
+  shrink_items<TI, NB, WAVES>(a, seg_ptrs(a.seg, a.T), red);
 }
 
 // Small batches (T <= 256 rows, pools of at most 1024 slots): the segment
@@ -157,7 +158,14 @@ hipError_t launch_shrink(const lora_pool_t& pool, int32_t* seg, int T, const Lau
   if (sh.grid <= 0 || T == 0) return hipSuccess;
   with_nb(sh.nb, [&](auto nb_c) {
     constexpr int NB = decltype(nb_c)::value;
-    if (pool.dtype == LORA_BF16)
+    // bf16 items of four rank blocks (long batches of mostly full row
+    // tiles) run in 8-wave workgroups, two per CU: an item is bound by its
+    // latency, and the second workgroup's items overlap it (prefill batch
+    // 42.9 -> 36.8 us in the bench; narrower items keep 16 waves, which
+    // measured faster for them)
+    if (pool.dtype == LORA_BF16 && NB == 4)
+      hipLaunchKernelGGL((shrink_mfma_kernel<uint16_t, NB, kWaves / 2>), dim3(sh.grid), dim3(kThreads / 2), 0, st, a);
+    else if (pool.dtype == LORA_BF16)
       hipLaunchKernelGGL((shrink_mfma_kernel<uint16_t, NB>), dim3(sh.grid), dim3(kThreads), 0, st, a);
     else
       hipLaunchKernelGGL((shrink_mfma_kernel<float, NB>), dim3(sh.grid), dim3(kThreads), 0, st, a);
