@@ -40,6 +40,18 @@ def row_rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max()) if len(num) else 0.0
 
 
+def row_rel_magnitude(got: np.ndarray, ref: np.ndarray, mag: np.ndarray) -> float:
+    """Largest per-row error relative to the row's magnitude: `mag` holds the
+    same sums taken over absolute values, the scale that fp32 rounding of the
+    row's sums is relative to.  A row whose sums cancel to a small result is
+    then held to the rounding its terms allow, not to its own size (mag is
+    never smaller than the result)."""
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(mag, axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float((num / den).max()) if len(num) else 0.0
+
+
 class DevProjection:
     """One projection of a workload on the device.
 

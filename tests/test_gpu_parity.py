@@ -21,7 +21,8 @@ if not torch.cuda.is_available():      # collected on CPU-only hosts, never run 
 import adapter_gemm_amd as agm
 import oracle
 from lora_inputs import make_workload
-from gpu_helpers import (DEV, DevProjection, segments, split_seg, rel_l2, row_rel_l2, to_f64, bf16_dev)
+from gpu_helpers import (DEV, DevProjection, segments, split_seg, rel_l2, row_rel_l2, row_rel_magnitude, to_f64,
+                         bf16_dev)
 
 TOL = {"fp32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
 
@@ -67,6 +68,15 @@ PIPE = {
 
 def _tol(p):
     return TOL["fp8"] if p.base_dtype == "fp8" else TOL[p.data_dtype]
+
+
+def _delta_magnitude(dp, w):
+    """The adapter term's sums over absolute values, row by row
+    (|s| |B| (|A| |x|)): per-row checks of the adapter term alone take their
+    scale from it, since a rank-1 row whose v cancels to nearly zero is small
+    while its rounding is set by the terms it sums."""
+    x, ids, act, A, B, rank, scale = dp.oracle_args(w)
+    return oracle.lora_delta(np.abs(x), ids, act, np.abs(A), np.abs(B), rank, np.abs(scale))
 
 
 def _v_ref(dp, w, segd):
@@ -234,7 +244,7 @@ def test_shrink_expand_parity(name):
         live = oracle.live_rows(w.ids, w.active)
         tol = _tol(p)
         assert rel_l2(d_got, d_ref) <= tol
-        assert row_rel_l2(d_got[live], d_ref[live]) <= tol
+        assert row_rel_magnitude(d_got[live], d_ref[live], _delta_magnitude(dp, w)[live]) <= tol
         assert np.all(d_got[~live] == 0)                 # rows not live untouched
 
 
@@ -1121,7 +1131,7 @@ def test_random_shapes_segments_shrink_expand(i):
     tol = _tol(p)
     if live.any():
         assert rel_l2(d_got, d_ref) <= tol
-        assert row_rel_l2(d_got[live], d_ref[live]) <= tol
+        assert row_rel_magnitude(d_got[live], d_ref[live], _delta_magnitude(dp, w)[live]) <= tol
     assert np.all(d_got[~live] == 0)
 
 
